@@ -1,0 +1,10 @@
+"""CPU fp64 oracle for the exact attention forward.
+
+TEST INFRASTRUCTURE ONLY: only tests/, the smoke check in __graft_entry__ and the
+benchmark's cpu_baseline leg may import it.  The HIP library never does, and
+this package imports nothing from the library (numpy only).
+"""
+from .attention import attention_ref, attention_ref_bhnd
+from .tiled import tiled_ref
+
+__all__ = ["attention_ref", "attention_ref_bhnd", "tiled_ref"]
