@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--sweep]
+
+A step is one fa_fwd call (the whole hot path: one kernel) over the workload's
+synthetic inputs, already resident in device memory.  Prints ONE JSON line:
+metric = forward TFLOP/s with 4*B*H*N^2*D FLOPs (halved when causal), the
+roofline of the kernel (its FLOPs per launch over its mean launch time from HIP
+events on the launch stream, against the bf16 dense MFMA peak), and the CPU
+fp64 oracle timed on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd attention TFLOP/s (4BHN²D, ÷2 causal) + % of bf16 MFMA peak, N=4096 D=128"
+# MI355X published dense peaks (TFLOP/s): bf16 MFMA 2516.6 (= 2.5 PFLOP/s), fp32 MFMA 157.3
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+KERNEL_SOURCES = ["exact_attention_65_amd/csrc/fa_fwd_kernel.hpp", "exact_attention_65_amd/csrc/fa_fwd.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_bf16_d128_b2_h32_n4096.txt")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none for this workload or the kernel source changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            m = re.match(r"^(\w+):\s*(.+?)\s*$", line)
+            if m:
+                kv[m.group(1)] = m.group(2)
+    if kv.get("workload") != workload or kv.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The fp64 oracle on whole (b, h) heads of the workload until the budget is spent."""
+    import numpy as np
+    import fa_inputs as fi
+    from oracle import attention_ref
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t_total = 0.0
+    for b, h in heads:
+        q, k, v = fi.head_qkv(w, b, h)
+        t0 = time.perf_counter()
+        attention_ref(q, k, v, w.causal, w.scale)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    flops = w.flops / (w.B * w.H) * done
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (b,h) heads of {w.name}, every query row, numpy float64 "
+                      f"({t_total:.2f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="bf16_b2_h32_n4096_d128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="one line per workload instead of the headline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (3 times), the known-size "
+                         "reference that scales the HBM byte counters")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the attention forward "
+                                   "shards over (batch, head) with no exchange, so N GPUs run N "
+                                   "independent copies", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import exact_attention_65_amd as fa
+    import fa_inputs as fi
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    names = [w.name for w in fi.ALL_WORKLOADS] if args.sweep else [args.workload]
+    for name in names:
+        w = fi.workload_by_name(name)
+        dt = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32
+        tensors = []
+        for t in (fi.T_Q, fi.T_K, fi.T_V):
+            bits = fi.full_tensor(w, t)
+            x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" \
+                else torch.from_numpy(bits)
+            tensors.append(x.cuda())
+            del bits, x
+        q, k, v = tensors
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+        stream = torch.cuda.current_stream()
+        sp = stream.cuda_stream
+
+        def step():
+            st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           w.B, w.H, w.N, w.D, w.causal, w.scale, dt, sp)
+            if st != fa.FA_OK:
+                raise fa.FaError(st)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+
+        # timed region: K back-to-back steps, events on the launch stream
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        region_ms = ev0.elapsed_time(ev1)
+        ms_per_step = region_ms / args.steps
+
+        # per-launch durations (each launch bracketed by its own events)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        launch_ms = np.array([a.elapsed_time(b) for a, b in evs])
+        kernel_ms = float(launch_ms.mean())
+
+        tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[w.dtype]
+        achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+        rec = {
+            "metric": METRIC,
+            "value": round(tflops, 2),
+            "unit": "TFLOP/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": w.dtype,
+            "data": "synthetic: seeded iid N(0,1) inputs"
+                    + (" with Q, K x4 (peaked)" if w.variant == fi.PEAKED else "")
+                    + (" rounded to bf16" if w.dtype == "bf16" else ""),
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+                       "causal": w.causal, "scale": w.scale, "parallelism": "single GPU",
+                       "pct_of_peak": round(100 * tflops / peak, 2),
+                       "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+                       "launch_ms_min": round(float(launch_ms.min()), 5),
+                       "launch_ms_median": round(float(np.median(launch_ms)), 5)},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                         "traffic": read_traffic(w.name)},
+        }
+        if not args.no_cpu_baseline and not args.sweep:
+            del q, k, v, o, lse
+            torch.cuda.empty_cache()
+            rec["cpu_baseline"] = cpu_baseline(w)
+        print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,127 @@
+"""Python binding of the MI355X exact-attention forward library (include/fa.h).
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels of libfa_mi355x.so.  The names mirror the C ABI (fa_fwd, fa_fwd_query,
+fa_status_str, fa_abi_version); ``attention_forward`` is the torch-facing
+helper that allocates O and LSE with torch and passes torch's current stream.
+
+The library is loaded on first use; if it has not been built
+(``python -m exact_attention_65_amd.build``) that use raises ImportError.
+There is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+from .build import LIB_PATH
+
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+
+FA_OK = 0
+FA_ERR_NULL_POINTER = 1
+FA_ERR_BAD_SHAPE = 2
+FA_ERR_BAD_SCALE = 3
+FA_ERR_BAD_DTYPE = 4
+FA_ERR_MISALIGNED = 5
+FA_ERR_ALIASING = 6
+FA_ERR_UNSUPPORTED = 7
+FA_ERR_HIP = 8
+
+EXPORTED = ("fa_fwd", "fa_fwd_query", "fa_status_str", "fa_abi_version")
+
+
+class FaSizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("q_bytes", "k_bytes", "v_bytes", "o_bytes", "lse_bytes", "workspace_bytes")]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(fa_status_str(status))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m exact_attention_65_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                           ctypes.c_int, vp]
+    lib.fa_fwd_query.restype = ctypes.c_int
+    lib.fa_fwd_query.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(FaSizes)]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_status_str.argtypes = [ctypes.c_int]
+    lib.fa_abi_version.restype = ctypes.c_int
+    lib.fa_abi_version.argtypes = []
+    return lib
+
+
+_LIB = None
+library_path = LIB_PATH
+
+
+def lib():
+    """The loaded ctypes library (loads it on first call)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, stream) -> int:
+    """Raw C call: pointers as integers (device addresses), returns the fa_status."""
+    return lib().fa_fwd(q, k, v, o, lse, B, H, N, D, int(causal), float(scale), int(dtype), stream)
+
+
+def fa_fwd_query(B, H, N, D, causal, dtype):
+    """Returns (status, FaSizes)."""
+    sz = FaSizes()
+    st = lib().fa_fwd_query(B, H, N, D, int(causal), int(dtype), ctypes.byref(sz))
+    return st, sz
+
+
+def fa_status_str(status: int) -> str:
+    return lib().fa_status_str(int(status)).decode()
+
+
+def fa_abi_version() -> int:
+    return lib().fa_abi_version()
+
+
+def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
+                      out=None, lse=None, stream=None):
+    """O, LSE = attention(q, k, v) for torch tensors [B, H, N, D] on a GPU.
+
+    q, k, v: contiguous, same shape, dtype torch.bfloat16 or torch.float32.
+    Returns (o, lse): o like q, lse float32 [B, H, N].  Launches on ``stream``
+    (default: torch's current stream) and does not synchronise.
+    """
+    import torch
+    if q.dtype == torch.bfloat16:
+        dt = FA_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = FA_DTYPE_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for x in (q, k, v):
+        if x.dtype != q.dtype or x.shape != q.shape or not x.is_cuda or not x.is_contiguous():
+            raise ValueError("q, k, v must be contiguous GPU tensors of one shape and dtype")
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H, N, D, causal, scale, dt, stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return out, lse

@@ -1,0 +1,27 @@
+// Host-side argument validation for fa_fwd / fa_fwd_query.  Pure C++: no HIP
+// header, no device access, so it can be compiled and tested on any host.
+#pragma once
+
+#include "fa.h"
+
+namespace fa {
+
+// Largest number of workgroups one launch may use (grid x dimension).
+constexpr int64_t kMaxGrid = 2147483647;
+// Query rows per workgroup of every kernel.
+constexpr int64_t kRowsPerBlock = 128;
+
+// Element size of a dtype, 0 if the dtype is unknown.
+size_t elem_size(int dtype);
+
+// Shape/dtype validation shared by both entry points; fills sizes on success.
+fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, fa_sizes* sizes);
+
+// Whether a valid shape is one the kernels are built for.
+fa_status check_supported(int64_t B, int64_t H, int64_t N, int64_t D);
+
+// Full validation of an fa_fwd call, without touching the device.
+fa_status check_call(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t D, float scale, int dtype);
+
+}  // namespace fa

@@ -1,0 +1,126 @@
+"""Helpers of the GPU parity tests: seeded inputs on the device, the HIP call,
+and the comparison with the fp64 oracle at the tolerances of the contract.
+
+Tolerances (O against the oracle on the same rounded inputs; LSE absolute):
+  float32 inputs: max |dO| <= 1e-5, |dLSE| <= 1e-3
+  bf16 inputs:    max |dO| <= 2e-2 and mean |dO| <= 2e-3, |dLSE| <= 1e-3
+
+The float32 bound is the one stated for the float32 workload, whose largest
+|scaled score| is about 5.  An fp32 score carries an absolute rounding error
+proportional to its magnitude, and a score error e moves the output by at most
+about 2 e max|v|, so inputs built with larger scores (a large scale, a constant
+shift of the scores) get the bound scaled by max|score| / 5 (``score_ratio``).
+"""
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+import torch
+
+import exact_attention_65_amd as fa
+import fa_inputs as fi
+from oracle import attention_ref
+
+TOL = {
+    "f32": dict(o_max=1e-5, o_mean=None, lse=1e-3),
+    "bf16": dict(o_max=2e-2, o_mean=2e-3, lse=1e-3),
+}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def log(msg: str):
+    sys.__stderr__.write(msg + "\n")
+    sys.__stderr__.flush()
+
+
+def record(entry: dict):
+    path = os.environ.get("FA_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(entry) + "\n")
+
+
+def to_device_bits(arr: np.ndarray, dtype: str) -> torch.Tensor:
+    """Raw element bits (uint16 for bf16, float32) -> device tensor of that dtype."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.cuda()
+
+
+def to_device_values(x: np.ndarray, dtype: str) -> torch.Tensor:
+    """float32 values exactly representable in dtype -> device tensor of that dtype."""
+    if dtype == "bf16":
+        return to_device_bits(fi.bf16_bits(np.asarray(x, dtype=np.float32)), dtype)
+    return to_device_bits(np.asarray(x, dtype=np.float32), dtype)
+
+
+def workload_tensors(w: fi.Workload):
+    return tuple(to_device_bits(fi.full_tensor(w, t), w.dtype) for t in (fi.T_Q, fi.T_K, fi.T_V))
+
+
+def run(q, k, v, causal, scale, stream=None):
+    o, lse = fa.attention_forward(q, k, v, causal=causal, scale=scale, stream=stream)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def errors(o_gpu, lse_gpu, o_ref, lse_ref):
+    do = np.abs(np.asarray(o_gpu, dtype=np.float64) - o_ref)
+    dl = np.abs(np.asarray(lse_gpu, dtype=np.float64) - lse_ref)
+    return dict(o_max=float(do.max()) if do.size else 0.0, o_mean=float(do.mean()) if do.size else 0.0,
+                lse_max=float(dl.max()) if dl.size else 0.0,
+                finite=bool(np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu))))
+
+
+F32_SCORE_REF = 5.0
+
+
+def score_ratio(q, k, scale, causal) -> float:
+    """max |scale * q.k| over visible pairs, relative to the float32 workload's ~5."""
+    s = np.abs(float(scale) * (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T))
+    if causal:
+        s = np.tril(s)
+    return max(1.0, float(s.max()) / F32_SCORE_REF)
+
+
+def assert_within(err: dict, dtype: str, what: str, f32_ratio: float = 1.0):
+    t = dict(TOL[dtype])
+    if dtype == "f32":
+        t["o_max"] *= f32_ratio
+    record(dict(case=what, dtype=dtype, **err))
+    log(f"  {what}: max|dO|={err['o_max']:.3e} mean|dO|={err['o_mean']:.3e} max|dLSE|={err['lse_max']:.3e}"
+        + (f" (f32 bound x{f32_ratio:.1f})" if dtype == "f32" and f32_ratio != 1.0 else ""))
+    assert err["finite"], f"{what}: non-finite output"
+    assert err["o_max"] <= t["o_max"], f"{what}: max|dO| {err['o_max']} > {t['o_max']}"
+    if t["o_mean"] is not None:
+        assert err["o_mean"] <= t["o_mean"], f"{what}: mean|dO| {err['o_mean']} > {t['o_mean']}"
+    assert err["lse_max"] <= t["lse"], f"{what}: max|dLSE| {err['lse_max']} > {t['lse']}"
+
+
+def compare_heads(w: fi.Workload, o, lse, heads, rows_for=None, what=""):
+    """Oracle on the given (b, h) pairs (all rows, or rows_for(h)) vs the device result."""
+    o_err, l_err = [], []
+    n_el = 0
+    mean_acc = 0.0
+    for b, h in heads:
+        q, k, v = fi.head_qkv(w, b, h)
+        rows = None if rows_for is None else rows_for(h)
+        o_ref, lse_ref = attention_ref(q, k, v, w.causal, w.scale, rows=rows)
+        og = o[b, h].float().cpu().numpy()
+        lg = lse[b, h].cpu().numpy()
+        if rows is not None:
+            og, lg = og[rows], lg[rows]
+        e = errors(og, lg, o_ref, lse_ref)
+        assert e["finite"], f"{what} (b={b}, h={h}): non-finite output"
+        o_err.append(e["o_max"])
+        l_err.append(e["lse_max"])
+        mean_acc += e["o_mean"] * o_ref.size
+        n_el += o_ref.size
+    err = dict(o_max=max(o_err), o_mean=mean_acc / n_el, lse_max=max(l_err), finite=True)
+    assert_within(err, w.dtype, what or w.name)
+    return err

@@ -1,0 +1,138 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and
+validates arguments before touching any device (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_65_amd as fa
+from exact_attention_65_amd import build as fab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def gpu_visible() -> bool:
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(fab.LIB_PATH):
+        fab.build()
+    return fab.LIB_PATH
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(fa.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(fab.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fab.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (fa_\w+)$", out, flags=re.M))
+    assert exported == set(declared_functions())
+
+
+def test_version_and_strings():
+    assert fa.fa_abi_version() == 1
+    for st in range(9):
+        s = fa.fa_status_str(st)
+        assert s.startswith("FA_")
+    assert fa.fa_status_str(99) == "unknown fa_status"
+
+
+def test_query_sizes():
+    st, sz = fa.fa_fwd_query(2, 32, 4096, 128, 0, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK
+    assert sz.q_bytes == sz.k_bytes == sz.v_bytes == sz.o_bytes == 2 * 32 * 4096 * 128 * 2
+    assert sz.lse_bytes == 2 * 32 * 4096 * 4 and sz.workspace_bytes == 0
+    st, sz = fa.fa_fwd_query(1, 8, 131072, 128, 1, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK and sz.workspace_bytes == 0
+    st, sz = fa.fa_fwd_query(1, 1, 256, 64, 0, fa.FA_DTYPE_F32)
+    assert st == fa.FA_OK and sz.q_bytes == 256 * 64 * 4
+    assert fa.fa_fwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_query(1, 1, 1 << 24, 128, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_query(0, 1, 256, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
+    assert fa.fa_fwd_query(1, 1, -3, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
+    assert fa.fa_fwd_query(1 << 40, 1 << 40, 256, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
+    assert fa.fa_fwd_query(1, 1, 256, 64, 0, 7)[0] == fa.FA_ERR_BAD_DTYPE
+    assert fa.lib().fa_fwd_query(1, 1, 256, 64, 0, 1, None) == fa.FA_ERR_NULL_POINTER
+    # too many workgroups for one launch
+    assert fa.fa_fwd_query(1 << 20, 1 << 10, 256, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+
+
+# fake, never-dereferenced addresses: validation rejects these calls on the host
+A = 1 << 20
+SZ = 1 << 20  # spacing of the fake buffers: larger than any tensor used below
+
+
+def call(q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, lse=A + 4 * SZ, B=1, H=2, N=100, D=64,
+         causal=0, scale=0.125, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_fwd(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), fa.FA_ERR_NULL_POINTER),
+    (dict(lse=0), fa.FA_ERR_NULL_POINTER),
+    (dict(N=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(B=-1), fa.FA_ERR_BAD_SHAPE),
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE),
+    (dict(scale=float("inf")), fa.FA_ERR_BAD_SCALE),
+    (dict(dtype=5), fa.FA_ERR_BAD_DTYPE),
+    (dict(k=A + SZ + 8), fa.FA_ERR_MISALIGNED),
+    (dict(lse=A + 4 * SZ + 4), fa.FA_ERR_MISALIGNED),
+    (dict(o=A + SZ), fa.FA_ERR_ALIASING),               # o on top of k
+    (dict(lse=A + 3 * SZ + 16), fa.FA_ERR_ALIASING),    # lse inside o
+    (dict(o=A + 2 * SZ + 2 * 100 * 64 * 2 - 16), fa.FA_ERR_ALIASING),  # o starts in v's last 16 bytes
+    (dict(o=A + 2 * SZ + 2 * 100 * 64 * 2), fa.FA_ERR_HIP),  # o right after v: valid
+    (dict(lse=A), fa.FA_ERR_ALIASING),                  # lse on top of q
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=32), fa.FA_ERR_UNSUPPORTED),
+])
+def test_validation_before_any_device_call(kw, expect):
+    if expect == fa.FA_ERR_HIP and gpu_visible():
+        pytest.skip("valid arguments would launch on fake addresses when a GPU is visible")
+    assert call(**kw) == expect
+
+
+def test_inputs_may_alias_each_other():
+    # q = k = v is valid; with no GPU visible the call then fails at the device query
+    if gpu_visible():
+        pytest.skip("valid arguments would launch on fake addresses when a GPU is visible")
+    assert call(k=A, v=A) == fa.FA_ERR_HIP
+
+
+def test_valid_call_without_device_reports_hip_error():
+    if gpu_visible():
+        pytest.skip("a GPU is visible here")
+    assert call() == fa.FA_ERR_HIP
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        fa.attention_forward(q, q, q)
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.attention_forward(q, q, q)  # CPU tensors
+
+
+@pytest.mark.slow
+def test_device_code_has_no_packed_fp32_and_no_spills_in_bf16():
+    asm = fab.device_asm()
+    assert not re.search(r"v_pk_(add|mul|fma)_f32", asm)
+    for m in re.finditer(r"\.name:\s+(\S+)\n(?:.*\n){0,12}?\s+\.vgpr_spill_count:\s+(\d+)", asm):
+        if "bf16" in m.group(1):
+            assert int(m.group(2)) == 0, m.group(1)
