@@ -51,6 +51,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 struct FwdArgs {
   const void* q;
@@ -93,21 +95,41 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
-
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Lane i and lane i^32 hold the two halves of one query's keys.  v_permlane32_swap
+// exchanges lanes 32-63 of its first operand with lanes 0-31 of its second;
+// applied to two copies of x, one copy ends up holding x of lanes 0-31 in both
+// halves and the other x of lanes 32-63, so their max / sum is the pair's.
+// Written as inline asm: this compiler folds the builtin's two results into one
+// when both operands start from the same value.  The s_nop gives the two wait
+// states a VALU write needs before v_permlane32_swap reads it.
+__device__ __forceinline__ void swap_halves(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float pair_max(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap_halves(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap_halves(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
 
 // ---------------------------------------------------------------------------
 // Online-softmax update for one tile.  s[] holds the raw scores of this lane's
 // query (masked ones -inf); afterwards s[] holds p = exp2(c*s - m_ref).  The
-// caller adds this tile's p to the running sum l (after any rescale of l here).
+// caller adds this tile's p to the running sums l and l2 (after any rescale of
+// them here).
 template <int NS>
 __device__ __forceinline__ void online_softmax(float (&s)[NS], float c, float& m_ref, float& l,
-                                               float& alpha_out, bool& rescaled) {
+                                               float& l2, float& alpha_out, bool& rescaled) {
   float mx = s[0];
 #pragma unroll
   for (int i = 1; i < NS; ++i) mx = fmaxf(mx, s[i]);
-  mx = fmaxf(mx, wave_xor32(mx));  // the other half-wave holds the other keys of this query
+  mx = pair_max(mx);  // the other half-wave holds the other keys of this query
   const float mt = mx * c;         // -inf when every key of the tile is masked for this row
   const bool need = mt > m_ref + kTau;
   rescaled = false;
@@ -117,6 +139,7 @@ __device__ __forceinline__ void online_softmax(float (&s)[NS], float c, float& m
     const float alpha = m_new == neg_inf() ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
     m_ref = m_new;
     l *= alpha;
+    l2 *= alpha;
     alpha_out = alpha;
     rescaled = true;
   }
@@ -127,22 +150,49 @@ __device__ __forceinline__ void online_softmax(float (&s)[NS], float c, float& m
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
+//
+// LDS: four static 64-key tiles (K and V, double buffered), row-major.  The
+// 16-byte chunk index of each row is XORed with a function of the row so that
+// the MFMA operand reads hit distinct banks (checked for 32- and 64-bank LDS):
+//   K (read 16 B per lane, 32 rows x 1 chunk):        kswz(row)
+//   V (read transposed, 8 B per lane, 4 rows x 32 B):  vswz(key & 3)
+// Tiles arrive by buffer loads straight into LDS (no registers, no VALU): each
+// lane's byte offset inside a tile is fixed, the tile start lives in the buffer
+// descriptor, and rows past N fall outside the descriptor's range.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (D == 128) return swap23(row & 15);
+  else return ((row ^ (row >> 2)) & 1) | (row & 2) | ((row >> 1) & 4);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int key) {
+  const int r = key & 3;
+  if constexpr (D == 128) return 4 * r | (r & 2);
+  else return 2 * r;
+}
+
+// Raw buffer descriptor word 3 for gfx9-family: 32-bit data format, no swizzle.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// 16 bytes per lane from buffer r at byte offset voff into LDS: the wave's 64
+// lanes fill the 1 KB at lds in lane order.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, u32x4* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int BN = 64;                 // keys per tile
-  constexpr int KCH = D / 8;             // 16-byte chunks per K row
-  constexpr int VCH = BN / 8;            // 16-byte chunks per V^T row
-  constexpr int K_CHUNKS = BN * KCH;     // chunks per K tile
-  constexpr int V_CHUNKS = D * VCH;      // chunks per V^T tile
-  constexpr int BUF = K_CHUNKS + V_CHUNKS;
-  constexpr int NKLD = K_CHUNKS / kThreads;          // K chunks each thread stages
-  constexpr int NVG = (BN / 4) * KCH;                // 4-key x 8-d groups per V tile
-  constexpr int NVLD = (NVG + kThreads - 1) / kThreads;
-  constexpr int NKB = BN / 32;                       // 32-key MFMA blocks per tile
-  constexpr int NDB = D / 32;                        // 32-wide d blocks of O
-  static_assert(K_CHUNKS % kThreads == 0, "K tile staging");
+  constexpr int BN = 64;                // keys per tile
+  constexpr int RB = D * 2;             // bytes per row
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int RPB = 64 / CPR;         // rows per 1 KB block (one wave-wide load)
+  constexpr int TILE16 = BN * CPR;      // 16-byte chunks per tile
+  constexpr int NLD = TILE16 / 64 / 4;  // 1 KB loads per wave per tile
+  constexpr int NKB = BN / 32;          // 32-key MFMA blocks per tile
+  constexpr int NDB = D / 32;           // 32-wide d blocks of O
+  static_assert(NLD >= 1, "tile loads");
 
-  __shared__ u32x4 smem[2 * BUF];
+  __shared__ u32x4 kA[TILE16], kB[TILE16], vA[TILE16], vB[TILE16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -165,6 +215,15 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
   const int qrow = q0 + wave * 32 + c32;  // this lane's query row
   const int wave_q0 = q0 + wave * 32;
 
+  // zero the tiles once: rows past N are never loaded, so they must hold finite values
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = tid; i < TILE16; i += kThreads) {
+      kA[i] = z; kB[i] = z; vA[i] = z; vB[i] = z;
+    }
+  }
+
   // Q fragments: B operand of the score MFMA, Q[qrow][16kk + 8h .. +7]
   bf16x8 qf[D / 16];
   {
@@ -177,62 +236,46 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
-  u32x4 kst[NKLD];
-  u32x4 vst[NVLD][4];
+  // per-lane byte offsets of the tile loads (fixed for every tile)
+  uint32_t koff[NLD], voff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int row = (wave * NLD + i) * RPB + lane / CPR;
+    const int cl = lane % CPR;
+    koff[i] = row * RB + ((cl ^ kswz<D>(row)) * 16);
+    voff[i] = row * RB + ((cl ^ vswz<D>(row)) * 16);
+  }
+  // per-lane LDS read addresses (bytes): K rows 32kb + swap23(c32), chunk 2kk + h
+  uint32_t kaddr[D / 16];
+  {
+    const int row = swap23(c32);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) kaddr[kk] = row * RB + (((2 * kk + h) ^ kswz<D>(row)) * 16);
+  }
+  // V^T operand by transposed reads: within each 16-lane group, lane 4r+q
+  // addresses row r (key 16c + 8h + 4s + r), columns 32db + 16gg + 4q .. +3
+  uint32_t vaddr[NDB];
+  {
+    const int g = lane >> 4, i16 = lane & 15;
+    const int hh = g >> 1, gg = g & 1, r = i16 >> 2, q = i16 & 3;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int chunk = 4 * db + 2 * gg + (q >> 1);
+      vaddr[db] = (8 * hh + r) * RB + ((chunk ^ vswz<D>(r)) * 16) + (q & 1) * 8;
+    }
+  }
 
-  auto load_tile = [&](int kv0) {
+  auto issue = [&](u32x4* kd, u32x4* vd, int kv0) {
+    const uint32_t bytes = (uint32_t)(N - kv0) * RB;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (size_t)kv0 * D), (short)0, (int)bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + (size_t)kv0 * D), (short)0, (int)bytes, kRsrcWord3);
 #pragma unroll
-    for (int r = 0; r < NKLD; ++r) {
-      const int id = tid + kThreads * r;
-      const int row = id / KCH, cc = id % KCH;
-      // rows past N read row N-1 instead: their scores are masked, their p is 0
-      const int key = min(kv0 + row, N - 1);
-      kst[r] = *(const u32x4*)(Kg + (size_t)key * D + cc * 8);
-    }
-#pragma unroll
-    for (int r = 0; r < NVLD; ++r) {
-      const int g = tid + kThreads * r;
-      if (NVG % kThreads == 0 || g < NVG) {
-        const int dc = g % KCH, kg = g / KCH;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = min(kv0 + 4 * kg + i, N - 1);
-          vst[r][i] = *(const u32x4*)(Vg + (size_t)key * D + dc * 8);
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    u32x4* Ks = smem + buf * BUF;
-#pragma unroll
-    for (int r = 0; r < NKLD; ++r) {
-      const int id = tid + kThreads * r;
-      const int row = id / KCH, cc = id % KCH;
-      Ks[row * KCH + (cc ^ (row & (KCH - 1)))] = kst[r];
-    }
-    char* Vs = (char*)(Ks + K_CHUNKS);
-#pragma unroll
-    for (int r = 0; r < NVLD; ++r) {
-      const int g = tid + kThreads * r;
-      if (NVG % kThreads == 0 || g < NVG) {
-        const int dc = g % KCH, kg = g / KCH;
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const int w = dd >> 1;
-          uint32_t lo, hi;
-          if (dd & 1) {
-            lo = (vst[r][0][w] >> 16) | (vst[r][1][w] & 0xFFFF0000u);
-            hi = (vst[r][2][w] >> 16) | (vst[r][3][w] & 0xFFFF0000u);
-          } else {
-            lo = (vst[r][0][w] & 0xFFFFu) | (vst[r][1][w] << 16);
-            hi = (vst[r][2][w] & 0xFFFFu) | (vst[r][3][w] << 16);
-          }
-          const int d = 8 * dc + dd;
-          const int chunk = (kg >> 1) ^ ((d ^ (d >> 3)) & 7);
-          *(u32x2*)(Vs + (d * VCH + chunk) * 16 + (kg & 1) * 8) = u32x2{lo, hi};
-        }
-      }
+    for (int i = 0; i < NLD; ++i) {
+      const int blk = wave * NLD + i;
+      lds_load16(kr, kd + blk * 64, koff[i]);
+      lds_load16(vr, vd + blk * 64, voff[i]);
     }
   };
 
@@ -241,21 +284,15 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
-  float m_ref = neg_inf(), l = 0.0f;
+  // l sums the bf16-rounded p the MFMA consumes, so the weights applied to V sum
+  // to exactly l; lx sums the fp32 p for the log-sum-exp.
+  float m_ref = neg_inf(), l = 0.0f, lx = 0.0f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int kv0 = j * BN;
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(kv0 + BN);
-
-    const u32x4* Ks = smem + buf * BUF;
-    const u32x4* Vs = Ks + K_CHUNKS;
+  auto compute = [&](const u32x4* Kt, const u32x4* Vt, int kv0) {
+    if (CAUSAL && kv0 > wave_q0 + 31) return;  // no key of this tile is visible to this wave
+    const char* kt = (const char*)Kt;
+    const char* vt = (const char*)Vt;
 
     // S^T = K Q^T for 64 keys x this wave's 32 queries
     f32x16 sacc[NKB];
@@ -267,8 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
     for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const int row = 32 * kb + swap23(c32);
-        const u32x4 kx = Ks[row * KCH + ((2 * kk + h) ^ (row & (KCH - 1)))];
+        const u32x4 kx = *(const u32x4*)(kt + kaddr[kk] + kb * 32 * RB);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[kk],
                                                            sacc[kb], 0, 0, 0);
       }
@@ -280,67 +316,89 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb * 16 + i] = sacc[kb][i];
 
-    // mask: keys past N, and keys after the query under the causal mask
+    // mask: keys past N, and keys after the query under the causal mask.
+    // Element (kb, i) of this lane holds key kv0 + 32kb + 8h + kofs(i).
     const bool tail = kv0 + BN > N;
     const bool diag = CAUSAL && (kv0 + BN - 1 > wave_q0);
     if (tail || diag) {
+      const int lim = (CAUSAL ? min(N - 1, qrow) : N - 1) - kv0 - 8 * h;  // visible iff offset <= lim
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + 32 * kb + swap23(8 * (i >> 2) + 4 * h + (i & 3));
-          if (key >= N || (CAUSAL && key > qrow)) s[kb * 16 + i] = neg_inf();
+          const int kofs = 32 * kb + 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
+          if (kofs > lim) s[kb * 16 + i] = neg_inf();
         }
     }
 
     float alpha;
     bool rescaled;
-    online_softmax(s, a.c, m_ref, l, alpha, rescaled);
+    online_softmax(s, a.c, m_ref, l, lx, alpha, rescaled);
     if (rescaled) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     }
+    {
+      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < NKB * 16; ++i) ps[i & 3] += s[i];
+      lx += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
 
     // P^T fragments: chunk c covers keys 16c .. 16c+15; this lane holds keys 16c + 8h + 0..7.
-    // The running sum adds the bf16-rounded p that the MFMA consumes, so the
-    // weights applied to V sum to exactly l.
     bf16x8 pf[BN / 16];
     float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int c = 0; c < BN / 16; ++c) {
       const int base = (c >> 1) * 16 + (c & 1) * 8;
-      u32x4 x;
+      // each packed word is a scalar before it is bit-cast: this compiler
+      // miscompiles __builtin_bit_cast applied to an element of a vector variable
+      uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = pack_bf16(s[base + 2 * e], s[base + 2 * e + 1]);
-        lsum[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[e]), ones, lsum[e], false);
+        w[e] = pack_bf16(s[base + 2 * e], s[base + 2 * e + 1]);
+        lsum[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, lsum[e], false);
       }
+      const u32x4 x = {w[0], w[1], w[2], w[3]};
       pf[c] = __builtin_bit_cast(bf16x8, x);
     }
     l += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T; V^T fragments by two transposed 8-byte reads
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int d = 32 * db + c32;
-      const int sw = (d ^ (d >> 3)) & 7;
 #pragma unroll
       for (int c = 0; c < BN / 16; ++c) {
-        const u32x4 vx = Vs[d * VCH + ((2 * c + h) ^ sw)];
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vx), pf[c], o[db],
-                                                        0, 0, 0);
+        const char* p = vt + vaddr[db] + 16 * c * RB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 4 * RB));
+        const i16x8 vx = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vx), pf[c], o[db], 0, 0, 0);
       }
     }
+  };
 
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+  __syncthreads();  // zeroed tiles visible before any load lands
+  if (n_tiles > 0) issue(kA, vA, 0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; j += 2) {
+    if (j + 1 < n_tiles) issue(kB, vB, (j + 1) * BN);
+    compute(kA, vA, j * BN);
     __syncthreads();
+    if (j + 1 < n_tiles) {
+      if (j + 2 < n_tiles) issue(kA, vA, (j + 2) * BN);
+      compute(kB, vB, (j + 1) * BN);
+      __syncthreads();
+    }
   }
 
-  // epilogue: O = o / l, LSE = (m + log2 l) ln 2
-  const float l_tot = l + wave_xor32(l);
+  // epilogue: O = o / l, LSE = (m + log2 lx) ln 2
+  const float l_tot = pair_sum(l);
+  const float lx_tot = pair_sum(lx);
   const float inv = 1.0f / l_tot;
   if (qrow < N) {
 #pragma unroll
@@ -352,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
                          pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
         *(u32x2*)(Og + (size_t)qrow * D + d) = w;
       }
-    if (h == 0) a.lse[(size_t)bh * N + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
+    if (h == 0) a.lse[(size_t)bh * N + qrow] = (m_ref + __log2f(lx_tot)) * kLn2;
   }
 }
 
@@ -467,7 +525,8 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fa_fwd_f32_kernel(
 
     float alpha;
     bool rescaled;
-    online_softmax(s, a.c, m_ref, l, alpha, rescaled);
+    float l_unused = 0.0f;  // P stays fp32 here: one sum serves both O and LSE
+    online_softmax(s, a.c, m_ref, l, l_unused, alpha, rescaled);
     if (rescaled) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -494,7 +553,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fa_fwd_f32_kernel(
     __syncthreads();
   }
 
-  const float l_tot = l + wave_xor32(l);
+  const float l_tot = pair_sum(l);
   const float inv = 1.0f / l_tot;
   if (qrow < N) {
 #pragma unroll

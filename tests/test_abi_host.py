@@ -136,3 +136,12 @@ def test_device_code_has_no_packed_fp32_and_no_spills_in_bf16():
     for m in re.finditer(r"\.name:\s+(\S+)\n(?:.*\n){0,12}?\s+\.vgpr_spill_count:\s+(\d+)", asm):
         if "bf16" in m.group(1):
             assert int(m.group(2)) == 0, m.group(1)
+
+
+def test_every_kernel_stub_is_defined():
+    """The host pass can silently drop a kernel's launch stub; the library must define all of them."""
+    out = subprocess.run(["nm", "-D", fab.LIB_PATH], capture_output=True, text=True).stdout
+    undefined = [l for l in out.splitlines() if " U " in l and "_ZN2fa" in l]
+    assert undefined == []
+    kernels = set(re.findall(r"(_ZN2fa\d+fa_fwd_\w+_kernelI\w+)", out))
+    assert len(kernels) == 8, kernels
