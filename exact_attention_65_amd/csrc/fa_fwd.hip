@@ -37,22 +37,25 @@ bool device_is_gfx950(int dev) {
 }
 
 template <typename Kern>
-hipError_t launch(Kern kern, const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(kern, dim3(a.n_blocks), dim3(kThreads), 0, stream, a);
+hipError_t launch(Kern kern, const FwdArgs& a, int threads, hipStream_t stream) {
+  hipLaunchKernelGGL(kern, dim3(a.n_blocks), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 
+// 256 threads and 128 query rows per workgroup for both element types
 hipError_t dispatch(int dtype, int D, bool causal, const FwdArgs& a, hipStream_t s) {
   if (dtype == FA_DTYPE_BF16) {
-    if (D == 128) return causal ? launch(fa_fwd_bf16_kernel<128, true>, a, s)
-                                : launch(fa_fwd_bf16_kernel<128, false>, a, s);
-    return causal ? launch(fa_fwd_bf16_kernel<64, true>, a, s)
-                  : launch(fa_fwd_bf16_kernel<64, false>, a, s);
+    const int t = kBF16Threads;
+    if (D == 128) return causal ? launch(fa_fwd_bf16_kernel<128, true>, a, t, s)
+                                : launch(fa_fwd_bf16_kernel<128, false>, a, t, s);
+    return causal ? launch(fa_fwd_bf16_kernel<64, true>, a, t, s)
+                  : launch(fa_fwd_bf16_kernel<64, false>, a, t, s);
   }
-  if (D == 128) return causal ? launch(fa_fwd_f32_kernel<128, true>, a, s)
-                              : launch(fa_fwd_f32_kernel<128, false>, a, s);
-  return causal ? launch(fa_fwd_f32_kernel<64, true>, a, s)
-                : launch(fa_fwd_f32_kernel<64, false>, a, s);
+  const int t = kThreads;
+  if (D == 128) return causal ? launch(fa_fwd_f32_kernel<128, true>, a, t, s)
+                              : launch(fa_fwd_f32_kernel<128, false>, a, t, s);
+  return causal ? launch(fa_fwd_f32_kernel<64, true>, a, t, s)
+                : launch(fa_fwd_f32_kernel<64, false>, a, t, s);
 }
 
 }  // namespace
@@ -75,7 +78,8 @@ extern "C" __attribute__((visibility("default"))) fa_status fa_fwd(
   a.o = o;
   a.lse = lse;
   a.n = (int)N;
-  a.n_qblk = (int)((N + fa::kBM - 1) / fa::kBM);
+  const int rows = dtype == FA_DTYPE_BF16 ? fa::kBF16Rows : fa::kBM;
+  a.n_qblk = (int)((N + rows - 1) / rows);
   a.n_blocks = (int)(B * H * a.n_qblk);
   const float c = std::fabs(scale) * 1.44269504088896340736f;
   a.c = c < FLT_MIN ? FLT_MIN : c;

@@ -1,6 +1,7 @@
 // Exact attention forward for CDNA4 (gfx950): one workgroup per (batch, head,
-// 128-row query block), online softmax over 64-key (bf16) or 32-key (fp32)
-// tiles held in LDS, both contractions on MFMA with fp32 accumulators.
+// query block of 256 rows in bf16, 128 in fp32), online softmax over 64-key
+// (bf16) or 32-key (fp32) tiles held in LDS, both contractions on MFMA with
+// fp32 accumulators.
 //
 // The method is the tiled loop of "Flash Attention" (wiki.ai-engineering.at),
 // section "Tiling Algorithm" — an outer loop over query blocks, an inner loop
@@ -15,7 +16,7 @@
 // einem Ausführungspfad"); only Q, K, V are read and only O and LSE written.
 //
 // Layout of the work (bf16):
-//   * 4 waves x 32 query rows.  Each wave computes S^T = K Q^T with
+//   * 8 waves x 32 query rows.  Each wave computes S^T = K Q^T with
 //     v_mfma_f32_32x32x16_bf16: keys on the MFMA rows, queries on the lanes.
 //     A lane then holds 16 scores of ONE query per 32-key block, so the row
 //     max is an in-register reduction plus one exchange with lane^32, and
@@ -28,8 +29,7 @@
 //   * K tiles are stored row-major in LDS with the 16-byte chunk index XORed by
 //     the row, V tiles transposed (V^T, [d][key]) with a chunk XOR by d, so the
 //     MFMA operand reads of 32 different rows hit distinct banks.  Tiles are
-//     double buffered: the global loads of tile j+1 are issued before tile j is
-//     consumed and written to the other buffer afterwards (one barrier per tile).
+//     double buffered and loaded while the previous tile is consumed.
 //   * The running reference max moves only when a row's tile max exceeds it by
 //     more than kTau (log2 units), so the output rescale is rare; the final
 //     o / l and LSE = (m + log2 l) ln 2 are exact for any reference <= max.
@@ -43,6 +43,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -52,7 +54,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 struct FwdArgs {
   const void* q;
@@ -61,7 +62,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   int n;          // sequence length N
-  int n_qblk;     // query blocks per (b, h): ceil(N / 128)
+  int n_qblk;     // query blocks per (b, h): ceil(N / rows per workgroup)
   int n_blocks;   // workgroups in the grid: B * H * n_qblk
   float c;        // |scale| * log2(e), at least FLT_MIN
   uint32_t qflip; // XOR mask applied to Q's bits: flips every sign when scale < 0
@@ -96,6 +97,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Pins a value in place: the empty asm "reads and rewrites" it, so its
+// computation cannot be moved past this point (the optimiser otherwise sinks
+// arithmetic toward its first use, out of the slot it was placed in).
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
 
 // Lane i and lane i^32 hold the two halves of one query's keys.  v_permlane32_swap
 // exchanges lanes 32-63 of its first operand with lanes 0-31 of its second;
@@ -153,12 +160,14 @@ __device__ __forceinline__ void online_softmax(float (&s)[NS], float c, float& m
 //
 // LDS: four static 64-key tiles (K and V, double buffered), row-major.  The
 // 16-byte chunk index of each row is XORed with a function of the row so that
-// the MFMA operand reads hit distinct banks (checked for 32- and 64-bank LDS):
+// the MFMA operand reads hit distinct banks:
 //   K (read 16 B per lane, 32 rows x 1 chunk):        kswz(row)
 //   V (read transposed, 8 B per lane, 4 rows x 32 B):  vswz(key & 3)
 // Tiles arrive by buffer loads straight into LDS (no registers, no VALU): each
 // lane's byte offset inside a tile is fixed, the tile start lives in the buffer
-// descriptor, and rows past N fall outside the descriptor's range.
+// descriptor, and rows past N fall outside the descriptor's range.  The V^T
+// operand of the value MFMA is read with the transposing LDS read
+// (ds_read_b64_tr_b16), which on this pattern runs near the plain read's rate.
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
   if constexpr (D == 128) return swap23(row & 15);
@@ -180,22 +189,53 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, u32x4* lds,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// Work split: 4 waves x 32 query rows (128 rows per workgroup), two
+// workgroups per CU (one wave of each per SIMD).  Each wave runs its own
+// software pipeline over the key tiles so that its matrix-core work and its
+// softmax arithmetic overlap inside the wave:
+//
+//   iteration j:  barrier ; DMA V_{j+1} and K_{j+2}
+//                 phase A: S_{j+1} = K_{j+1} Q^T  (MFMA)   ||  p = exp2(c s_j - m), P_j, sums
+//                 phase B: O^T += V_j^T P_j^T     (MFMA)   ||  mask / row max / reference of S_{j+1}
+//
+// The MFMAs of a phase do not depend on the arithmetic beside them, so the
+// two are issued in alternation: one MFMA runs 32 cycles on the matrix core
+// while the same wave issues the VALU work of its slot.  The output rescale
+// decided in phase B of iteration j is applied before the value MFMAs of
+// iteration j+1, after the ones it must not touch.  One barrier per tile: a
+// buffer is refilled only after every wave has finished the iteration that
+// read it, and everything issued at the top of iteration j is waited for by the
+// barrier of iteration j+1, a full iteration later.
+constexpr int kBF16Threads = 256;
+constexpr int kBF16Rows = 128;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
   constexpr int BN = 64;                // keys per tile
-  constexpr int RB = D * 2;             // bytes per row
+  constexpr int RB = D * 2;             // bytes per K / V row
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int RPB = 64 / CPR;         // rows per 1 KB block (one wave-wide load)
   constexpr int TILE16 = BN * CPR;      // 16-byte chunks per tile
-  constexpr int NLD = TILE16 / 64 / 4;  // 1 KB loads per wave per tile
+  constexpr int NLD = TILE16 / 64 / 4;  // 1 KB K loads per wave per tile
   constexpr int NKB = BN / 32;          // 32-key MFMA blocks per tile
   constexpr int NDB = D / 32;           // 32-wide d blocks of O
+  constexpr int NKK = D / 16;           // 16-deep steps of the score contraction
+  constexpr int NCC = BN / 16;          // 16-key steps of the value contraction
+  constexpr int NSA = NKK * NKB;        // score MFMAs per tile (phase A slots)
+  constexpr int NSB = NDB * NCC;        // value MFMAs per tile (phase B slots)
+  constexpr int PFA = 3;                // score-fragment reads in flight in phase A
+  constexpr int PFB = 4;                // value-fragment reads in flight in phase B
   static_assert(NLD >= 1, "tile loads");
+  static_assert(NSA == 16 && NSB == 16 || D == 64, "slot counts");
 
+  // four separate arrays, picked at compile time by the two-step unrolled loop:
+  // the compiler then sees that a tile load into one buffer cannot alias reads
+  // of another and does not wait for the load before those reads
   __shared__ u32x4 kA[TILE16], kB[TILE16], vA[TILE16], vB[TILE16];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
   const int N = a.n;
 
@@ -203,40 +243,46 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
   const int bh = t / a.n_qblk;
   int qb = t - bh * a.n_qblk;
   if (CAUSAL) qb = a.n_qblk - 1 - qb;  // longest query blocks first
-  const int q0 = qb * kBM;
+  const int q0 = qb * kBF16Rows;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + head;
   const uint16_t* __restrict__ Kg = (const uint16_t*)a.k + head;
   const uint16_t* __restrict__ Vg = (const uint16_t*)a.v + head;
   uint16_t* __restrict__ Og = (uint16_t*)a.o + head;
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
+  const int kv_end = CAUSAL ? min(N, q0 + kBF16Rows) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
   const int qrow = q0 + wave * 32 + c32;  // this lane's query row
   const int wave_q0 = q0 + wave * 32;
+  // tiles 0 .. n_vis-1 hold keys visible to some row of this wave
+  const int n_vis = CAUSAL ? min(n_tiles, (wave_q0 + 31) / BN + 1) : n_tiles;
 
   // zero the tiles once: rows past N are never loaded, so they must hold finite values
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = tid; i < TILE16; i += kThreads) {
-      kA[i] = z; kB[i] = z; vA[i] = z; vB[i] = z;
+    for (int i = tid; i < TILE16; i += kBF16Threads) {
+      kA[i] = z;
+      kB[i] = z;
+      vA[i] = z;
+      vB[i] = z;
     }
   }
 
-  // Q fragments: B operand of the score MFMA, Q[qrow][16kk + 8h .. +7]
-  bf16x8 qf[D / 16];
+  // Q fragments: B operand of the score MFMA, Q[qrow][16kk + 8h .. +7] (signs
+  // flipped for a negative scale)
+  bf16x8 qf[NKK];
   {
     const u32x4 flip = {a.qflip, a.qflip, a.qflip, a.qflip};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
+    for (int kk = 0; kk < NKK; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (qrow < N) x = *(const u32x4*)(Qg + (size_t)qrow * D + 16 * kk + 8 * h) ^ flip;
       qf[kk] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  // per-lane byte offsets of the tile loads (fixed for every tile)
+  // tile DMA: per-lane byte offsets (fixed for every tile)
   uint32_t koff[NLD], voff[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
@@ -245,155 +291,247 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
     koff[i] = row * RB + ((cl ^ kswz<D>(row)) * 16);
     voff[i] = row * RB + ((cl ^ vswz<D>(row)) * 16);
   }
-  // per-lane LDS read addresses (bytes): K rows 32kb + swap23(c32), chunk 2kk + h
-  uint32_t kaddr[D / 16];
-  {
-    const int row = swap23(c32);
+  auto issue = [&](u32x4* dst, const uint16_t* src, const uint32_t (&off)[NLD], int kv0)
+      __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(N - kv0) * RB), kRsrcWord3);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) kaddr[kk] = row * RB + (((2 * kk + h) ^ kswz<D>(row)) * 16);
-  }
-  // V^T operand by transposed reads: within each 16-lane group, lane 4r+q
-  // addresses row r (key 16c + 8h + 4s + r), columns 32db + 16gg + 4q .. +3
-  uint32_t vaddr[NDB];
-  {
-    const int g = lane >> 4, i16 = lane & 15;
-    const int hh = g >> 1, gg = g & 1, r = i16 >> 2, q = i16 & 3;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int chunk = 4 * db + 2 * gg + (q >> 1);
-      vaddr[db] = (8 * hh + r) * RB + ((chunk ^ vswz<D>(r)) * 16) + (q & 1) * 8;
-    }
-  }
-
-  auto issue = [&](u32x4* kd, u32x4* vd, int kv0) {
-    const uint32_t bytes = (uint32_t)(N - kv0) * RB;
-    const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (size_t)kv0 * D), (short)0, (int)bytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + (size_t)kv0 * D), (short)0, (int)bytes, kRsrcWord3);
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int blk = wave * NLD + i;
-      lds_load16(kr, kd + blk * 64, koff[i]);
-      lds_load16(vr, vd + blk * 64, voff[i]);
-    }
+    for (int i = 0; i < NLD; ++i) lds_load16(r, dst + (wave * NLD + i) * 64, off[i]);
   };
 
+  // per-lane LDS read addresses (bytes).  K operand of score slot (kk, kb): row
+  // 32kb + swap23(c32), chunk 2kk + h -> (kaddr0 ^ (kk << 5)) + kb * 32 * RB.
+  // V^T operand of value slot (db, cc) by two transposed reads: within each
+  // 16-lane group, lane 4r+q addresses row r (key 16cc + 8h + 4s + r),
+  // columns 32db + 16gg + 4q .. +3; d block db's address is the db = 0 address
+  // XOR (db << 6), key step cc adds 16 rows.
+  const uint32_t kaddr0 = [&] {
+    const int row = swap23(c32);
+    return (uint32_t)(row * RB + ((h ^ kswz<D>(row)) * 16));
+  }();
+  const uint32_t vaddr0 = [&] {
+    const int g = lane >> 4, i16 = lane & 15;
+    const int hh = g >> 1, gg = g & 1, r = i16 >> 2, q = i16 & 3;
+    const int chunk = 2 * gg + (q >> 1);
+    return (uint32_t)((8 * hh + r) * RB + ((chunk ^ vswz<D>(r)) * 16) + (q & 1) * 8);
+  }();
+  auto kfrag = [&](const u32x4* Kt, int s) __attribute__((always_inline)) {
+    const int kk = s / NKB, kb = s % NKB;
+    return *(const u32x4*)((const char*)Kt + (kaddr0 ^ (kk << 5)) + kb * 32 * RB);
+  };
+  auto vfrag = [&](const u32x4* Vt, int s) __attribute__((always_inline)) {
+    const int db = s % NDB, cc = s / NDB;
+    const char* p = (const char*)Vt + (vaddr0 ^ (db << 6)) + 16 * cc * RB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+    const i16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 4 * RB));
+    return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // state: o (unnormalised output), m_ref (running reference max, log2 units),
+  // l (sum of the bf16-rounded p: normalises O), lx (sum of fp32 p: LSE),
+  // pf (bf16 P^T of the tile whose values are next), a pending output rescale
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
-  // l sums the bf16-rounded p the MFMA consumes, so the weights applied to V sum
-  // to exactly l; lx sums the fp32 p for the log-sum-exp.
-  float m_ref = neg_inf(), l = 0.0f, lx = 0.0f;
+  f32x16 sA[NKB], sB[NKB];
+  bf16x8 pf[NCC];
+  float m_ref = neg_inf(), l = 0.0f, lx = 0.0f, mu = 0.0f;
+  bool pend = false;
+  float pend_alpha = 1.0f;
+  const float c = a.c;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  auto compute = [&](const u32x4* Kt, const u32x4* Vt, int kv0) {
-    if (CAUSAL && kv0 > wave_q0 + 31) return;  // no key of this tile is visible to this wave
-    const char* kt = (const char*)Kt;
-    const char* vt = (const char*)Vt;
-
-    // S^T = K Q^T for 64 keys x this wave's 32 queries
-    f32x16 sacc[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 kx = *(const u32x4*)(kt + kaddr[kk] + kb * 32 * RB);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[kk],
-                                                           sacc[kb], 0, 0, 0);
-      }
-    }
-
-    float s[NKB * 16];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb * 16 + i] = sacc[kb][i];
-
-    // mask: keys past N, and keys after the query under the causal mask.
-    // Element (kb, i) of this lane holds key kv0 + 32kb + 8h + kofs(i).
-    const bool tail = kv0 + BN > N;
-    const bool diag = CAUSAL && (kv0 + BN - 1 > wave_q0);
-    if (tail || diag) {
-      const int lim = (CAUSAL ? min(N - 1, qrow) : N - 1) - kv0 - 8 * h;  // visible iff offset <= lim
+  // ---- pieces of the softmax -------------------------------------------
+  // mask keys past N and, under the causal mask, after the query (only on the
+  // tiles that have such keys).  Element (kb, i) holds key kv0 + 32kb + 8h +
+  // kofs(i).
+  auto mask = [&](f32x16 (&s)[NKB], int j) __attribute__((always_inline)) {
+    const int kv0 = j * BN;
+    if (kv0 + BN > N || (CAUSAL && kv0 + BN - 1 > wave_q0)) {
+      const int lim = (CAUSAL ? min(N - 1, qrow) : N - 1) - kv0 - 8 * h;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kofs = 32 * kb + 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
-          if (kofs > lim) s[kb * 16 + i] = neg_inf();
+          if (kofs > lim) s[kb][i] = neg_inf();
         }
     }
+  };
+  // row max of the tile and the reference update: the wave moves its
+  // references only when some row's tile max exceeds its reference by more
+  // than kTau.  Split in slices so it can sit beside the value MFMAs:
+  // slice 0..NKB-1: partial max of block kb; slice NKB: the update.
+  float mpart[NKB];
+  auto ref_slice = [&](const f32x16 (&s)[NKB], int k) __attribute__((always_inline)) {
+    if (k < NKB) {
+      float mx = s[k][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[k][i]);
+      pin(mx);
+      mpart[k] = mx;
+    } else {
+      float mx = mpart[0];
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb) mx = fmaxf(mx, mpart[kb]);
+      mx = pair_max(mx);
+      const float mt = mx * c;
+      const bool any = __builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0;
+      const float m_new = any ? fmaxf(m_ref, mt) : m_ref;
+      const float alpha = m_new == neg_inf() ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l *= alpha;
+      lx *= alpha;
+      m_ref = m_new;
+      pend = any;
+      pend_alpha = alpha;
+      mu = m_new == neg_inf() ? 0.0f : m_new;
+      pin(mu);
+      pin(pend_alpha);
+      pin(l);
+      pin(lx);
+    }
+  };
+  // p = exp2(c s - mu) for the 8 scores of value step cc, their sums, and the
+  // bf16 P^T fragment of step cc (keys 16cc + 8h .. +7 of this lane's query)
+  float lsum[2] = {0.0f, 0.0f}, xsum[2] = {0.0f, 0.0f};
+  auto p_slice = [&](f32x16 (&s)[NKB], int cc, int half) __attribute__((always_inline)) {
+    const int kb = cc >> 1, base = (cc & 1) * 8 + 4 * half;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[kb][base + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][base + e], c, -mu));
+    // each packed word is a scalar before it is bit-cast: this compiler
+    // miscompiles __builtin_bit_cast applied to an element of a vector variable
+    const uint32_t w0 = pack_bf16(s[kb][base + 0], s[kb][base + 1]);
+    const uint32_t w1 = pack_bf16(s[kb][base + 2], s[kb][base + 3]);
+    lsum[half] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, lsum[half], false);
+    lsum[half] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, lsum[half], false);
+    xsum[half] += s[kb][base + 0] + s[kb][base + 1];
+    xsum[half] += s[kb][base + 2] + s[kb][base + 3];
+    uint32_t r0 = w0, r1 = w1;
+    pin(r0);
+    pin(r1);
+    pin(lsum[half]);
+    pin(xsum[half]);
+    return u32x2{r0, r1};
+  };
 
-    float alpha;
-    bool rescaled;
-    online_softmax(s, a.c, m_ref, l, lx, alpha, rescaled);
-    if (rescaled) {
+  // ---- phases --------------------------------------------------------------
+  // phase A of iteration j: score MFMAs of tile j+1 into sn beside the
+  // exponentials of tile j in sc: one slot per score MFMA (16 for D = 128, 8
+  // for D = 64), the 8 four-score p slices spread evenly over the slots.  K
+  // fragments are read PFA slots ahead; the last PFB slots also start the
+  // reads of phase B's first value fragments (from Vc) so that phase B does
+  // not begin by waiting on LDS.
+  auto phase_a = [&](f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], const u32x4* Kt, const u32x4* Vc,
+                     u32x4 (&vf)[NSB]) __attribute__((always_inline)) {
+    constexpr int NP = 2 * NCC;  // p slices (4 scores each)
+    constexpr int SLOTS = NSA > NP ? NSA : NP;
+    static_assert(PFB <= SLOTS && PFA <= NSA, "prefetch depths");
+    lsum[0] = lsum[1] = xsum[0] = xsum[1] = 0.0f;
+    u32x4 kf[NSA];
+#pragma unroll
+    for (int k = 0; k < PFA; ++k) kf[k] = kfrag(Kt, k);
+    u32x2 pw[NP];
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) {
+      if (k + PFA < NSA) kf[k + PFA] = kfrag(Kt, k + PFA);
+      if (k >= SLOTS - PFB) vf[k - (SLOTS - PFB)] = vfrag(Vc, k - (SLOTS - PFB));
+#pragma unroll
+      for (int q = k * NP / SLOTS; q < (k + 1) * NP / SLOTS; ++q) pw[q] = p_slice(sc, q >> 1, q & 1);
+      if (k < NSA) {
+        const int kk = k / NKB, kb = k % NKB;
+        const f32x16 z = {};
+        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[k]), qf[kk],
+                                                         kk == 0 ? z : sn[kb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+      const u32x4 x = {pw[2 * cc][0], pw[2 * cc][1], pw[2 * cc + 1][0], pw[2 * cc + 1][1]};
+      pf[cc] = __builtin_bit_cast(bf16x8, x);
+    }
+    l += lsum[0] + lsum[1];
+    lx += xsum[0] + xsum[1];
+  };
+  // phase B of iteration j: value MFMAs of tile j (V^T from Vt, P^T in pf;
+  // fragments 0 .. PFB-1 already requested in phase A) beside the reference
+  // update of tile j+1's scores in sn
+  auto phase_b = [&](const f32x16 (&sn)[NKB], const u32x4* Vt, u32x4 (&vf)[NSB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < NSB; ++k) {
+      if (k + PFB < NSB) vf[k + PFB] = vfrag(Vt, k + PFB);
+      // the reference slices go in the early slots so the update is known
+      // well before the next phase needs mu
+      if (k <= NKB) ref_slice(sn, k);
+      const int db = k % NDB, cc = k / NDB;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[k]), pf[cc], o[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto apply_rescale = [&]() __attribute__((always_inline)) {
+    if (pend) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    }
-    {
-      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int i = 0; i < NKB * 16; ++i) ps[i & 3] += s[i];
-      lx += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    }
-
-    // P^T fragments: chunk c covers keys 16c .. 16c+15; this lane holds keys 16c + 8h + 0..7.
-    bf16x8 pf[BN / 16];
-    float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int c = 0; c < BN / 16; ++c) {
-      const int base = (c >> 1) * 16 + (c & 1) * 8;
-      // each packed word is a scalar before it is bit-cast: this compiler
-      // miscompiles __builtin_bit_cast applied to an element of a vector variable
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w[e] = pack_bf16(s[base + 2 * e], s[base + 2 * e + 1]);
-        lsum[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, lsum[e], false);
-      }
-      const u32x4 x = {w[0], w[1], w[2], w[3]};
-      pf[c] = __builtin_bit_cast(bf16x8, x);
-    }
-    l += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-
-    // O^T += V^T P^T; V^T fragments by two transposed 8-byte reads
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int c = 0; c < BN / 16; ++c) {
-        const char* p = vt + vaddr[db] + 16 * c * RB;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
-        const i16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 4 * RB));
-        const i16x8 vx = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vx), pf[c], o[db], 0, 0, 0);
-      }
+        for (int i = 0; i < 16; ++i) o[db][i] *= pend_alpha;
+      pend = false;
     }
   };
 
-  __syncthreads();  // zeroed tiles visible before any load lands
-  if (n_tiles > 0) issue(kA, vA, 0);
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; j += 2) {
-    if (j + 1 < n_tiles) issue(kB, vB, (j + 1) * BN);
-    compute(kA, vA, j * BN);
-    __syncthreads();
-    if (j + 1 < n_tiles) {
-      if (j + 2 < n_tiles) issue(kA, vA, (j + 2) * BN);
-      compute(kB, vB, (j + 1) * BN);
-      __syncthreads();
+  // ---- prologue ------------------------------------------------------------
+  __syncthreads();  // zeroed K tiles visible before any load lands
+  if (n_tiles > 0) {
+    issue(kA, Kg, koff, 0);
+    issue(vA, Vg, voff, 0);
+  }
+  if (n_tiles > 1) issue(kB, Kg, koff, BN);
+  __syncthreads();  // K_0, K_1, V_0 in LDS
+  if (n_vis > 0) {
+    // scores of tile 0 and their reference (the running sums are still zero)
+#pragma unroll
+    for (int k = 0; k < NSA; ++k) {
+      const int kk = k / NKB, kb = k % NKB;
+      const f32x16 z = {};
+      sA[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kfrag(kA, k)), qf[kk],
+                                                       kk == 0 ? z : sA[kb], 0, 0, 0);
     }
+    mask(sA, 0);
+#pragma unroll
+    for (int k = 0; k <= NKB; ++k) ref_slice(sA, k);
+    pend = false;
+  }
+
+  // ---- main loop: iteration j consumes S_j (scores in sc) and V_j^T --------
+  // Buffers: K_{j+1} is in Kn, K_{j+2} goes to Kd (which held K_j), V_j is in
+  // Vc, V_{j+1} goes to Vd (which held V_{j-1}).
+  auto iteration = [&](int j, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], const u32x4* Kn, u32x4* Kd,
+                       const u32x4* Vc, u32x4* Vd) __attribute__((always_inline)) {
+    // Everyone is done with iteration j-1 and its tile loads have landed.  The
+    // explicit wait is required: at the barrier that heads the loop this
+    // compiler drops the wait for the loads issued in the previous iteration
+    // (it keeps it only at the barrier inside the loop body).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 < n_tiles) issue(Vd, Vg, voff, (j + 1) * BN);
+    if (j + 2 < n_tiles) issue(Kd, Kg, koff, (j + 2) * BN);
+    if (j >= n_vis) return;  // nothing of this tile or later is visible to this wave
+    // One code path for every iteration (a second one for the last tile costs
+    // more registers than the chip has): after the last visible tile the
+    // "next" scores are computed from whatever K buffer is there and then fully
+    // masked, which leaves the reference and the sums unchanged, and are never
+    // used.
+    u32x4 vf[NSB];
+    phase_a(sc, sn, Kn, Vc, vf);
+    apply_rescale();
+    mask(sn, j + 1);
+    phase_b(sn, Vc, vf);
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    iteration(j, sA, sB, kB, kA, vA, vB);
+    if (j + 1 < n_tiles) iteration(j + 1, sB, sA, kA, kB, vB, vA);
   }
 
   // epilogue: O = o / l, LSE = (m + log2 lx) ln 2
