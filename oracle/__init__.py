@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY: only tests/, the smoke check in __graft_entry__ and th
 benchmark's cpu_baseline leg may import it.  The HIP library never does, and
 this package imports nothing from the library (numpy only).
 """
-from .attention import attention_ref, attention_ref_bhnd
+from .attention import attention_ref, attention_ref_bhnd, merge_ref
 from .tiled import tiled_ref
 
-__all__ = ["attention_ref", "attention_ref_bhnd", "tiled_ref"]
+__all__ = ["attention_ref", "attention_ref_bhnd", "merge_ref", "tiled_ref"]

@@ -242,6 +242,30 @@ def pin_linear_in_values(attn):
         _close(o12, a * o1 + b * o2, tol=1e-12, what="linearity")
 
 
+# P14 ------------------------------------------------------------------------
+def pin_causal_query_suffix(attn):
+    """With fewer queries than keys the queries are the last positions of the
+    sequence: causal attention of Q against K equals the last Nq rows of the
+    square causal attention whose query rows are [P; Q], whatever P is; a single
+    query therefore sees every key."""
+    g = _rng(14)
+    nk, d = 23, 8
+    k, v = g.standard_normal((2, nk, d))
+    scale = 0.4
+    for nq in (1, 5, 22, nk):
+        q = g.standard_normal((nq, d))
+        full_q = np.concatenate([g.standard_normal((nk - nq, d)), q])
+        o_full, lse_full = attn(full_q, k, v, True, scale)[:2]
+        o, lse = attn(q, k, v, True, scale)[:2]
+        _close(o, o_full[nk - nq:], what=f"suffix nq={nq} o")
+        _close(lse, lse_full[nk - nq:], what=f"suffix nq={nq} lse")
+    q1 = g.standard_normal((1, d))
+    o_c, l_c = attn(q1, k, v, True, scale)[:2]
+    o_n, l_n = attn(q1, k, v, False, scale)[:2]
+    _close(o_c, o_n, what="single query o")
+    _close(l_c, l_n, what="single query lse")
+
+
 ALL_PINS = [
     pin_worked_examples,
     pin_uniform_scores,
@@ -254,4 +278,5 @@ ALL_PINS = [
     pin_mpmath_bruteforce,
     pin_causal_prefix,
     pin_linear_in_values,
+    pin_causal_query_suffix,
 ]

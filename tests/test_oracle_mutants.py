@@ -24,7 +24,8 @@ def _make(scores=None, mask=None, maxsub=True, axis=1, normalise=True, lse_fn=No
         rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
         s = scale * (scores(q[rows], k) if scores else q[rows] @ k.T)
         if causal:
-            bad = mask(rows, k.shape[0]) if mask else (np.arange(k.shape[0])[None, :] > rows[:, None])
+            nq, nk = q.shape[0], k.shape[0]
+            bad = mask(rows, nq, nk) if mask else (np.arange(nk)[None, :] > rows[:, None] + (nk - nq))
             s = np.where(bad, -np.inf, s)
         m = s.max(axis=axis, keepdims=True) if maxsub else np.zeros((1, 1))
         with np.errstate(all="ignore"):
@@ -46,9 +47,11 @@ MUTANTS = {
     "transposed_scores": _make(scores=lambda q, k: (k[: q.shape[0]] @ q.T).T if k.shape[0] >= q.shape[0] and q.shape[0] == k.shape[0] else q @ k.T * 1.0000001),
     "no_max_subtraction": _make(maxsub=False),
     "wrong_sign_scores": _make(scores=lambda q, k: -(q @ k.T)),
-    "causal_excludes_diagonal": _make(mask=lambda r, n: np.arange(n)[None, :] >= r[:, None]),
-    "causal_upper_triangle": _make(mask=lambda r, n: np.arange(n)[None, :] < r[:, None]),
-    "causal_off_by_one": _make(mask=lambda r, n: np.arange(n)[None, :] > r[:, None] + 1),
+    "causal_excludes_diagonal": _make(mask=lambda r, nq, nk: np.arange(nk)[None, :] >= r[:, None] + (nk - nq)),
+    "causal_upper_triangle": _make(mask=lambda r, nq, nk: np.arange(nk)[None, :] < r[:, None] + (nk - nq)),
+    "causal_off_by_one": _make(mask=lambda r, nq, nk: np.arange(nk)[None, :] > r[:, None] + (nk - nq) + 1),
+    "causal_offset_ignored": _make(mask=lambda r, nq, nk: np.arange(nk)[None, :] > r[:, None]),
+    "causal_offset_reversed": _make(mask=lambda r, nq, nk: np.arange(nk)[None, :] > r[:, None] - (nk - nq)),
     "softmax_over_queries": _make(axis=0),
     "no_normalisation": _make(normalise=False),
     "scale_dropped": _make(scale_fn=lambda s, d: 1.0),
