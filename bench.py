@@ -2,7 +2,7 @@
 """Benchmark of the exact-attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--sweep]
+                    [--split S] [--no-cpu-baseline] [--sweep]
 
 A step is one fa_fwd call (the whole hot path: one kernel) over the workload's
 synthetic inputs, already resident in device memory.  Prints ONE JSON line:
@@ -10,6 +10,12 @@ metric = forward TFLOP/s with 4*B*H*N^2*D FLOPs (halved when causal), the
 roofline of the kernel (its FLOPs per launch over its mean launch time from HIP
 events on the launch stream, against the bf16 dense MFMA peak), and the CPU
 fp64 oracle timed on a bounded sample of the same workload on this host.
+
+Workloads with fewer queries than keys (decode, chunked prefill), and any bf16
+workload run with --split S (S key ranges; 0 = the library's choice), step
+through fa_fwd_split: the range kernel and the merge kernel, both inside the
+timed events.  Their roofline is the HBM one (GB/s of Q, K, V, O and LSE) when
+the workload's arithmetic intensity is below the machine balance.
 """
 from __future__ import annotations
 
@@ -27,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd attention TFLOP/s (4BHN²D, ÷2 causal) + % of bf16 MFMA peak, N=4096 D=128"
 # MI355X published dense peaks (TFLOP/s): bf16 MFMA 2516.6 (= 2.5 PFLOP/s), fp32 MFMA 157.3
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 KERNEL_SOURCES = ["exact_attention_65_amd/csrc/fa_fwd_kernel.hpp", "exact_attention_65_amd/csrc/fa_fwd.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_bf16_d128_b2_h32_n4096.txt")
 
@@ -92,6 +99,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bf16_b2_h32_n4096_d128")
+    ap.add_argument("--split", type=int, default=None,
+                    help="run through fa_fwd_split with this many key ranges (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="one line per workload instead of the headline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -120,9 +129,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    names = [w.name for w in fi.ALL_WORKLOADS] if args.sweep else [args.workload]
+    names = [w.name for w in fi.ALL_WORKLOADS + fi.SPLIT_WORKLOADS] if args.sweep else [args.workload]
     for name in names:
         w = fi.workload_by_name(name)
+        split = args.split if args.split is not None else (fa.FA_SPLIT_AUTO if w.NQ > 0 else None)
+        if split is not None and w.dtype != "bf16":
+            continue
         dt = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32
         tensors = []
         for t in (fi.T_Q, fi.T_K, fi.T_V):
@@ -133,13 +145,24 @@ def main():
             del bits, x
         q, k, v = tensors
         o = torch.empty_like(q)
-        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+        lse = torch.empty((w.B, w.H, w.nq), dtype=torch.float32, device=q.device)
         stream = torch.cuda.current_stream()
         sp = stream.cuda_stream
+        n_ranges = 1
+        if split is not None:
+            st, sz, n_ranges = fa.fa_fwd_split_query(w.B, w.H, w.nq, w.N, w.D, w.causal, split, dt)
+            if st != fa.FA_OK:
+                raise fa.FaError(st)
+            ws = torch.empty(max(1, sz.workspace_bytes), dtype=torch.uint8, device=q.device)
 
         def step():
-            st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                           w.B, w.H, w.N, w.D, w.causal, w.scale, dt, sp)
+            if split is None:
+                st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               w.B, w.H, w.N, w.D, w.causal, w.scale, dt, sp)
+            else:
+                st = fa.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                     ws.data_ptr(), ws.numel(), w.B, w.H, w.nq, w.N, w.D, w.causal, w.scale,
+                                     split, dt, sp)
             if st != fa.FA_OK:
                 raise fa.FaError(st)
 
@@ -175,6 +198,17 @@ def main():
         tflops = w.flops / (ms_per_step * 1e-3) / 1e12
         peak = PEAK_TFLOPS[w.dtype]
         achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+        elt = 2 if w.dtype == "bf16" else 4
+        alg_bytes = w.kv_bytes + 2.0 * w.B * w.H * w.nq * w.D * elt + 4.0 * w.B * w.H * w.nq
+        hbm_bound = w.flops / alg_bytes < peak / PEAK_HBM_GBS * 1e3  # intensity below machine balance
+        if hbm_bound:
+            roofline = {"bound": "hbm", "achieved": round(alg_bytes / (kernel_ms * 1e-3) / 1e9, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(alg_bytes / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}
+        else:
+            roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(achieved / peak, 4),
+                        "traffic": read_traffic(w.name) if split is None else None}
         rec = {
             "metric": METRIC,
             "value": round(tflops, 2),
@@ -190,15 +224,14 @@ def main():
             "data": "synthetic: seeded iid N(0,1) inputs"
                     + (" with Q, K x4 (peaked)" if w.variant == fi.PEAKED else "")
                     + (" rounded to bf16" if w.dtype == "bf16" else ""),
-            "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "Nq": w.nq, "D": w.D,
                        "causal": w.causal, "scale": w.scale, "parallelism": "single GPU",
+                       "entry_point": "fa_fwd" if split is None else f"fa_fwd_split ({n_ranges} key ranges)",
                        "pct_of_peak": round(100 * tflops / peak, 2),
                        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
                        "launch_ms_min": round(float(launch_ms.min()), 5),
                        "launch_ms_median": round(float(np.median(launch_ms)), 5)},
-            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                         "traffic": read_traffic(w.name)},
+            "roofline": roofline,
         }
         if not args.no_cpu_baseline and not args.sweep:
             del q, k, v, o, lse

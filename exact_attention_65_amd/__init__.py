@@ -2,8 +2,10 @@
 
 Argument marshalling only: every step of the attention runs in the HIP
 kernels of libfa_mi355x.so.  The names mirror the C ABI (fa_fwd, fa_fwd_query,
-fa_status_str, fa_abi_version); ``attention_forward`` is the torch-facing
-helper that allocates O and LSE with torch and passes torch's current stream.
+fa_fwd_split, fa_fwd_split_query, fa_status_str, fa_abi_version);
+``attention_forward`` and ``attention_forward_split`` are the torch-facing
+helpers that allocate O, LSE (and the split workspace) with torch and pass
+torch's current stream.
 
 The library is loaded on first use; if it has not been built
 (``python -m exact_attention_65_amd.build``) that use raises ImportError.
@@ -29,8 +31,13 @@ FA_ERR_MISALIGNED = 5
 FA_ERR_ALIASING = 6
 FA_ERR_UNSUPPORTED = 7
 FA_ERR_HIP = 8
+FA_ERR_WORKSPACE = 9
 
-EXPORTED = ("fa_fwd", "fa_fwd_query", "fa_status_str", "fa_abi_version")
+FA_SPLIT_AUTO = 0
+FA_SPLIT_MAX = 256
+
+EXPORTED = ("fa_fwd", "fa_fwd_query", "fa_fwd_split", "fa_fwd_split_query", "fa_status_str",
+            "fa_abi_version")
 
 
 class FaSizes(ctypes.Structure):
@@ -54,6 +61,12 @@ def _load():
                            ctypes.c_int, vp]
     lib.fa_fwd_query.restype = ctypes.c_int
     lib.fa_fwd_query.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(FaSizes)]
+    lib.fa_fwd_split.restype = ctypes.c_int
+    lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64,
+                                 ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_fwd_split_query.restype = ctypes.c_int
+    lib.fa_fwd_split_query.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(FaSizes), ctypes.POINTER(ctypes.c_int)]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_abi_version.restype = ctypes.c_int
@@ -83,6 +96,22 @@ def fa_fwd_query(B, H, N, D, causal, dtype):
     sz = FaSizes()
     st = lib().fa_fwd_query(B, H, N, D, int(causal), int(dtype), ctypes.byref(sz))
     return st, sz
+
+
+def fa_fwd_split(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, D, causal, scale, n_splits,
+                 dtype, stream) -> int:
+    """Raw C call: pointers as integers (device addresses), returns the fa_status."""
+    return lib().fa_fwd_split(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, D, int(causal),
+                              float(scale), int(n_splits), int(dtype), stream)
+
+
+def fa_fwd_split_query(B, H, Nq, Nk, D, causal, n_splits, dtype):
+    """Returns (status, FaSizes, number of key ranges)."""
+    sz = FaSizes()
+    splits = ctypes.c_int(0)
+    st = lib().fa_fwd_split_query(B, H, Nq, Nk, D, int(causal), int(n_splits), int(dtype), ctypes.byref(sz),
+                                  ctypes.byref(splits))
+    return st, sz, splits.value
 
 
 def fa_status_str(status: int) -> str:
@@ -122,6 +151,47 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                 B, H, N, D, causal, scale, dt, stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return out, lse
+
+
+def attention_forward_split(q, k, v, causal: bool = False, scale: float | None = None,
+                            n_splits: int = FA_SPLIT_AUTO, out=None, lse=None, workspace=None, stream=None):
+    """O, LSE = attention(q, k, v) through fa_fwd_split, for bf16 torch tensors.
+
+    q: [B, H, Nq, D], k and v: [B, H, Nk, D] (contiguous, one dtype, on a GPU).
+    Under the causal mask the queries are the last Nq positions (Nq <= Nk).
+    Allocates the workspace with torch unless one (a uint8 GPU tensor) is given.
+    Launches on ``stream`` (default: torch's current stream); no synchronisation.
+    """
+    import torch
+    if q.dtype != torch.bfloat16:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for x in (q, k, v):
+        if x.dtype != q.dtype or not x.is_cuda or not x.is_contiguous() or x.dim() != 4:
+            raise ValueError("q, k, v must be contiguous 4-D GPU tensors of one dtype")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, D] with q's B, H, D")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st, sz, splits = fa_fwd_split_query(B, H, Nq, Nk, D, causal, n_splits, FA_DTYPE_BF16)
+    if st != FA_OK:
+        raise FaError(st)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None and sz.workspace_bytes > 0:
+        workspace = torch.empty(sz.workspace_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
+                      B, H, Nq, Nk, D, causal, scale, n_splits, FA_DTYPE_BF16, stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st)
     return out, lse

@@ -72,9 +72,103 @@ fa_status check_call(const void* q, const void* k, const void* v, const void* o,
   return check_supported(B, H, N, D);
 }
 
+// Number of key ranges: the requested count, or for FA_SPLIT_AUTO enough for
+// about 512 workgroups in all (two per CU on 256 CUs: one round, so the merge
+// reads few partials), but no more than leaves 8 key tiles of 64 per
+// range, keeps the partial results (Nq rows of D+1 floats per range) within a
+// quarter of the K/V bytes (S <= Nk / (4 Nq)), and at most 64.  Square shapes
+// therefore stay on one range: their partial results would double the traffic.
+static int resolve_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int requested) {
+  if (requested != FA_SPLIT_AUTO) return requested;
+  const int64_t blocks = B * H * ((Nq + kRowsPerBlock - 1) / kRowsPerBlock);
+  const int64_t tiles = (Nk + kKeysPerTile - 1) / kKeysPerTile;
+  int64_t s = (512 + blocks - 1) / blocks;
+  if (s > tiles / 8) s = tiles / 8;
+  if (s > Nk / (4 * Nq)) s = Nk / (4 * Nq);
+  if (s > 64) s = 64;
+  return s < 1 ? 1 : (int)s;
+}
+
+fa_status check_split_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
+                            int n_splits, int dtype, fa_sizes* sizes, int* splits) {
+  const size_t elt = elem_size(dtype);
+  if (elt == 0) return FA_ERR_BAD_DTYPE;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || D <= 0) return FA_ERR_BAD_SHAPE;
+  if (causal && Nq > Nk) return FA_ERR_BAD_SHAPE;
+  if (n_splits < 0 || n_splits > FA_SPLIT_MAX) return FA_ERR_BAD_SHAPE;
+  uint64_t bh, qrows, krows, qel, kel, qbytes, kbytes, lbytes;
+  if (!mul_ok((uint64_t)B, (uint64_t)H, &bh) || !mul_ok(bh, (uint64_t)Nq, &qrows) ||
+      !mul_ok(bh, (uint64_t)Nk, &krows) || !mul_ok(qrows, (uint64_t)D, &qel) ||
+      !mul_ok(krows, (uint64_t)D, &kel) || !mul_ok(qel, elt, &qbytes) || !mul_ok(kel, elt, &kbytes) ||
+      !mul_ok(qrows, 4, &lbytes))
+    return FA_ERR_BAD_SHAPE;
+  if (qbytes > (uint64_t)SIZE_MAX || kbytes > (uint64_t)SIZE_MAX) return FA_ERR_BAD_SHAPE;
+  // the arguments are valid; what follows decides whether the kernels support them
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (Nq * D > (int64_t)INT32_MAX || Nk * D > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
+  const int64_t qblocks = (Nq + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (B > kMaxGrid / H || B * H > kMaxGrid / qblocks) return FA_ERR_UNSUPPORTED;
+  const int s = resolve_splits(B, H, Nq, Nk, n_splits);
+  if (B * H * qblocks > kMaxGrid / s) return FA_ERR_UNSUPPORTED;
+  uint64_t ws = 0;
+  if (s > 1 && (!mul_ok(qrows, (uint64_t)(D + 1) * 4, &ws) || !mul_ok(ws, (uint64_t)s, &ws)))
+    return FA_ERR_BAD_SHAPE;
+  if (ws > (uint64_t)SIZE_MAX) return FA_ERR_BAD_SHAPE;
+  if (sizes) {
+    sizes->q_bytes = sizes->o_bytes = (size_t)qbytes;
+    sizes->k_bytes = sizes->v_bytes = (size_t)kbytes;
+    sizes->lse_bytes = (size_t)lbytes;
+    sizes->workspace_bytes = (size_t)ws;
+  }
+  if (splits) *splits = s;
+  return FA_OK;
+}
+
+fa_status check_split_call(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                           const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                           int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int n_splits,
+                           int dtype, int* splits) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
+  fa_sizes sz;
+  int s = 1;
+  // invalid arguments first; a valid but unsupported shape is reported after them
+  fa_status st = check_split_shape(B, H, Nq, Nk, D, causal, n_splits, dtype, &sz, &s);
+  if (st != FA_OK && st != FA_ERR_UNSUPPORTED) return st;
+  if (!std::isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (st == FA_ERR_UNSUPPORTED) return st;
+  const bool ws = sz.workspace_bytes > 0;
+  if (ws && !workspace) return FA_ERR_NULL_POINTER;
+  const void* ptrs[6] = {q, k, v, o, lse, ws ? workspace : q};
+  for (const void* p : ptrs)
+    if ((uintptr_t)p % 16 != 0) return FA_ERR_MISALIGNED;
+  if (workspace_bytes < sz.workspace_bytes) return FA_ERR_WORKSPACE;
+  // outputs and workspace may not overlap inputs or each other
+  struct Buf { const void* p; size_t n; };
+  const Buf outs[3] = {{o, sz.o_bytes}, {lse, sz.lse_bytes}, {workspace, ws ? sz.workspace_bytes : 0}};
+  const Buf ins[3] = {{q, sz.q_bytes}, {k, sz.k_bytes}, {v, sz.v_bytes}};
+  for (int i = 0; i < 3; ++i) {
+    if (outs[i].n == 0) continue;
+    for (int j = i + 1; j < 3; ++j)
+      if (outs[j].n && overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return FA_ERR_ALIASING;
+    for (const Buf& b : ins)
+      if (overlaps(outs[i].p, outs[i].n, b.p, b.n)) return FA_ERR_ALIASING;
+  }
+  if (splits) *splits = s;
+  return FA_OK;
+}
+
 }  // namespace fa
 
 extern "C" {
+
+__attribute__((visibility("default"))) fa_status fa_fwd_split_query(int64_t B, int64_t H, int64_t Nq,
+                                                                     int64_t Nk, int64_t D, int causal,
+                                                                     int n_splits, fa_dtype dtype,
+                                                                     fa_sizes* out, int* splits_out) {
+  if (!out) return FA_ERR_NULL_POINTER;
+  return fa::check_split_shape(B, H, Nq, Nk, D, causal, n_splits, (int)dtype, out, splits_out);
+}
 
 __attribute__((visibility("default"))) fa_status fa_fwd_query(int64_t B, int64_t H, int64_t N,
                                                                int64_t D, int causal,
@@ -98,6 +192,7 @@ __attribute__((visibility("default"))) const char* fa_status_str(fa_status s) {
     case FA_ERR_UNSUPPORTED:
       return "FA_ERR_UNSUPPORTED: needs D in {64,128}, N*D < 2^31, at most 2^31-1 workgroups, a gfx950 device";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call failed";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace_bytes is smaller than the call needs";
   }
   return "unknown fa_status";
 }

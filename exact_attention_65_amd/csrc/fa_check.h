@@ -24,4 +24,17 @@ fa_status check_supported(int64_t B, int64_t H, int64_t N, int64_t D);
 fa_status check_call(const void* q, const void* k, const void* v, const void* o, const void* lse,
                      int64_t B, int64_t H, int64_t N, int64_t D, float scale, int dtype);
 
+// Keys per tile of the bf16 kernel (the unit a key range is made of).
+constexpr int64_t kKeysPerTile = 64;
+
+// fa_fwd_split_query: sizes and the resolved number of key ranges.
+fa_status check_split_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
+                            int n_splits, int dtype, fa_sizes* sizes, int* splits);
+
+// Full validation of an fa_fwd_split call, without touching the device.
+fa_status check_split_call(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                           const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                           int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int n_splits,
+                           int dtype, int* splits);
+
 }  // namespace fa

@@ -1,11 +1,16 @@
-// Host launcher and C entry point of the attention forward (see include/fa.h).
+// Host launchers and C entry points of the attention forward (see include/fa.h).
 //
-// One kernel launch per call: a 1-D grid of B*H*ceil(N/128) workgroups of 256
+// fa_fwd: one kernel launch, a 1-D grid of B*H*ceil(N/128) workgroups of 256
 // threads, each computing one 128-row query block of one (batch, head) — the
 // outer loop over query blocks of the tiled algorithm in "Flash Attention"
 // (wiki.ai-engineering.at), section "Tiling Algorithm".  Under the causal mask
 // a query block only visits key tiles up to its last row, so tiles above the
 // diagonal are never loaded or computed.
+//
+// fa_fwd_split: the same kernel with the key tiles of each query block divided
+// into n_splits contiguous ranges (one workgroup each, writing fp32 partial
+// results to the caller's workspace), then a merge kernel on the same stream;
+// with one range, a single launch writing O and LSE.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -37,25 +42,69 @@ bool device_is_gfx950(int dev) {
 }
 
 template <typename Kern>
-hipError_t launch(Kern kern, const FwdArgs& a, int threads, hipStream_t stream) {
-  hipLaunchKernelGGL(kern, dim3(a.n_blocks), dim3(threads), 0, stream, a);
+hipError_t launch(Kern kern, int blocks, const FwdArgs& a, int threads, hipStream_t stream) {
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 
-// 256 threads and 128 query rows per workgroup for both element types
-hipError_t dispatch(int dtype, int D, bool causal, const FwdArgs& a, hipStream_t s) {
-  if (dtype == FA_DTYPE_BF16) {
-    const int t = kBF16Threads;
-    if (D == 128) return causal ? launch(fa_fwd_bf16_kernel<128, true>, a, t, s)
-                                : launch(fa_fwd_bf16_kernel<128, false>, a, t, s);
-    return causal ? launch(fa_fwd_bf16_kernel<64, true>, a, t, s)
-                  : launch(fa_fwd_bf16_kernel<64, false>, a, t, s);
-  }
-  const int t = kThreads;
-  if (D == 128) return causal ? launch(fa_fwd_f32_kernel<128, true>, a, t, s)
-                              : launch(fa_fwd_f32_kernel<128, false>, a, t, s);
-  return causal ? launch(fa_fwd_f32_kernel<64, true>, a, t, s)
-                : launch(fa_fwd_f32_kernel<64, false>, a, t, s);
+// bf16 attention kernel for (D, causal, split); 256 threads, 128 query rows
+template <bool SPLIT>
+hipError_t launch_bf16(int D, bool causal, const FwdArgs& a, hipStream_t s) {
+  const int t = kBF16Threads, n = a.n_blocks;
+  if (D == 128) return causal ? launch(fa_fwd_bf16_kernel<128, true, SPLIT>, n, a, t, s)
+                              : launch(fa_fwd_bf16_kernel<128, false, SPLIT>, n, a, t, s);
+  return causal ? launch(fa_fwd_bf16_kernel<64, true, SPLIT>, n, a, t, s)
+                : launch(fa_fwd_bf16_kernel<64, false, SPLIT>, n, a, t, s);
+}
+
+// fp32 attention kernel; 256 threads and 128 query rows per workgroup
+hipError_t launch_f32(int D, bool causal, const FwdArgs& a, hipStream_t s) {
+  const int t = kThreads, n = a.n_blocks;
+  if (D == 128) return causal ? launch(fa_fwd_f32_kernel<128, true>, n, a, t, s)
+                              : launch(fa_fwd_f32_kernel<128, false>, n, a, t, s);
+  return causal ? launch(fa_fwd_f32_kernel<64, true>, n, a, t, s)
+                : launch(fa_fwd_f32_kernel<64, false>, n, a, t, s);
+}
+
+// merge of the key ranges: one lane group per output row
+hipError_t launch_combine(int D, const FwdArgs& a, hipStream_t s) {
+  const long long rows = (long long)a.n_bh * a.nq;
+  const int per_block = kCombineThreads / (D / 8);
+  const int blocks = (int)((rows + per_block - 1) / per_block);
+  if (D == 128) return launch(fa_combine_kernel<128>, blocks, a, kCombineThreads, s);
+  return launch(fa_combine_kernel<64>, blocks, a, kCombineThreads, s);
+}
+
+// Arguments shared by both entry points.  scale: |scale| log2(e) for exp2, the
+// sign applied to Q's bits.
+FwdArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                  int64_t Nq, int64_t Nk, float scale, int dtype, int rows, int splits) {
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.nq = (int)Nq;
+  a.nk = (int)Nk;
+  a.n_bh = (int)(B * H);
+  a.n_qblk = (int)((Nq + rows - 1) / rows);
+  a.n_split = splits;
+  a.n_blocks = (int)(B * H * a.n_qblk * splits);
+  const float c = std::fabs(scale) * 1.44269504088896340736f;
+  a.c = c < FLT_MIN ? FLT_MIN : c;
+  a.qflip = 0u;
+  if (std::signbit(scale) && scale != 0.0f) a.qflip = dtype == FA_DTYPE_BF16 ? 0x80008000u : 0x80000000u;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
+  return a;
+}
+
+fa_status device_check() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (!device_is_gfx950(dev)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
 }
 
 }  // namespace
@@ -66,28 +115,33 @@ extern "C" __attribute__((visibility("default"))) fa_status fa_fwd(
     int64_t N, int64_t D, int causal, float scale, fa_dtype dtype, fa_stream_t stream) {
   fa_status st = fa::check_call(q, k, v, o, lse, B, H, N, D, scale, (int)dtype);
   if (st != FA_OK) return st;
+  if ((st = fa::device_check()) != FA_OK) return st;
 
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
-  if (!fa::device_is_gfx950(dev)) return FA_ERR_UNSUPPORTED;
+  const bool bf16 = dtype == FA_DTYPE_BF16;
+  const fa::FwdArgs a =
+      fa::make_args(q, k, v, o, lse, B, H, N, N, scale, (int)dtype, bf16 ? fa::kBF16Rows : fa::kBM, 1);
+  const hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = bf16 ? fa::launch_bf16<false>((int)D, causal != 0, a, s)
+                            : fa::launch_f32((int)D, causal != 0, a, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
 
-  fa::FwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.n = (int)N;
-  const int rows = dtype == FA_DTYPE_BF16 ? fa::kBF16Rows : fa::kBM;
-  a.n_qblk = (int)((N + rows - 1) / rows);
-  a.n_blocks = (int)(B * H * a.n_qblk);
-  const float c = std::fabs(scale) * 1.44269504088896340736f;
-  a.c = c < FLT_MIN ? FLT_MIN : c;
-  a.qflip = 0u;
-  if (std::signbit(scale) && scale != 0.0f)
-    a.qflip = dtype == FA_DTYPE_BF16 ? 0x80008000u : 0x80000000u;
+extern "C" __attribute__((visibility("default"))) fa_status fa_fwd_split(
+    const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+    size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
+    float scale, int n_splits, fa_dtype dtype, fa_stream_t stream) {
+  int splits = 1;
+  fa_status st = fa::check_split_call(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, D,
+                                      causal, scale, n_splits, (int)dtype, &splits);
+  if (st != FA_OK) return st;
+  if ((st = fa::device_check()) != FA_OK) return st;
 
-  if (fa::dispatch((int)dtype, (int)D, causal != 0, a, (hipStream_t)stream) != hipSuccess)
-    return FA_ERR_HIP;
-  return FA_OK;
+  fa::FwdArgs a = fa::make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, (int)dtype, fa::kBF16Rows, splits);
+  const hipStream_t s = (hipStream_t)stream;
+  if (splits == 1) return fa::launch_bf16<false>((int)D, causal != 0, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  // workspace: [splits][B*H][Nq][D] float outputs, then [splits][B*H][Nq] log-sum-exps
+  a.o_part = (float*)workspace;
+  a.lse_part = a.o_part + (size_t)splits * a.n_bh * a.nq * D;
+  if (fa::launch_bf16<true>((int)D, causal != 0, a, s) != hipSuccess) return FA_ERR_HIP;
+  return fa::launch_combine((int)D, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -61,11 +61,16 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  int n;          // sequence length N
-  int n_qblk;     // query blocks per (b, h): ceil(N / rows per workgroup)
-  int n_blocks;   // workgroups in the grid: B * H * n_qblk
+  int nq;         // query rows per (b, h)
+  int nk;         // key / value rows per (b, h); nq <= nk under the causal mask
+  int n_bh;       // B * H
+  int n_qblk;     // query blocks per (b, h): ceil(nq / rows per workgroup)
+  int n_split;    // workgroups that share the keys of one query block (bf16 only)
+  int n_blocks;   // workgroups in the grid: n_bh * n_qblk * n_split
   float c;        // |scale| * log2(e), at least FLT_MIN
   uint32_t qflip; // XOR mask applied to Q's bits: flips every sign when scale < 0
+  float* o_part;   // with n_split > 1: [n_split][n_bh][nq][D] fp32 outputs of each key range
+  float* lse_part; //                   [n_split][n_bh][nq] their log-sum-exps (-inf: no key)
 };
 
 constexpr int kThreads = 256;
@@ -209,7 +214,12 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, u32x4* lds,
 constexpr int kBF16Threads = 256;
 constexpr int kBF16Rows = 128;
 
-template <int D, bool CAUSAL>
+// SPLIT: the keys of each query block are divided into n_split contiguous
+// ranges of whole tiles, one workgroup each; a workgroup writes its rows'
+// normalised fp32 output and log-sum-exp over its range to o_part / lse_part,
+// and fa_combine_kernel merges them.  Without SPLIT the one workgroup of a query
+// block covers all its keys and writes O and LSE.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
   constexpr int BN = 64;                // keys per tile
   constexpr int RB = D * 2;             // bytes per K / V row
@@ -237,25 +247,36 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
-  const int N = a.n;
+  const int NQ = a.nq, NK = a.nk;
+  // query i is position i + OFF of the sequence: key j is visible iff j <= i + OFF
+  const int OFF = CAUSAL ? NK - NQ : 0;
 
+  // workgroup -> (b, h), query block, key range; consecutive ids share (b, h)
   const int t = xcd_remap(blockIdx.x, a.n_blocks);
-  const int bh = t / a.n_qblk;
-  int qb = t - bh * a.n_qblk;
+  const int per_bh = a.n_qblk * a.n_split;
+  const int bh = t / per_bh;
+  const int rem = t - bh * per_bh;
+  int qb = SPLIT ? rem / a.n_split : rem;
+  const int split = SPLIT ? rem - qb * a.n_split : 0;
   if (CAUSAL) qb = a.n_qblk - 1 - qb;  // longest query blocks first
   const int q0 = qb * kBF16Rows;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + head;
-  const uint16_t* __restrict__ Kg = (const uint16_t*)a.k + head;
-  const uint16_t* __restrict__ Vg = (const uint16_t*)a.v + head;
-  uint16_t* __restrict__ Og = (uint16_t*)a.o + head;
+  const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + (size_t)bh * NQ * D;
+  const uint16_t* __restrict__ Kg = (const uint16_t*)a.k + (size_t)bh * NK * D;
+  const uint16_t* __restrict__ Vg = (const uint16_t*)a.v + (size_t)bh * NK * D;
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBF16Rows) : N;
+  // key tiles of the query block: 0 .. n_tiles-1; this workgroup's: t_lo .. t_hi-1
+  const int kv_end = CAUSAL ? min(NK, q0 + kBF16Rows + OFF) : NK;
   const int n_tiles = (kv_end + BN - 1) / BN;
+  const int t_lo = SPLIT ? (int)((long long)n_tiles * split / a.n_split) : 0;
+  const int t_hi = SPLIT ? (int)((long long)n_tiles * (split + 1) / a.n_split) : n_tiles;
+  const int n_loc = t_hi - t_lo;         // tiles this workgroup loads
+  const int kv_lim = min(NK, t_hi * BN);  // keys past this one are outside the range
   const int qrow = q0 + wave * 32 + c32;  // this lane's query row
   const int wave_q0 = q0 + wave * 32;
-  // tiles 0 .. n_vis-1 hold keys visible to some row of this wave
-  const int n_vis = CAUSAL ? min(n_tiles, (wave_q0 + 31) / BN + 1) : n_tiles;
+  // tiles t_lo .. t_lo+n_vis-1 hold keys visible to some row of this wave (none
+  // when all its rows are past the last query)
+  const int wave_end = CAUSAL ? min(t_hi, (wave_q0 + 31 + OFF) / BN + 1) : t_hi;
+  const int n_vis = wave_q0 < NQ ? max(0, wave_end - t_lo) : 0;
 
   // zero the tiles once: rows past N are never loaded, so they must hold finite values
   {
@@ -277,7 +298,7 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < N) x = *(const u32x4*)(Qg + (size_t)qrow * D + 16 * kk + 8 * h) ^ flip;
+      if (qrow < NQ) x = *(const u32x4*)(Qg + (size_t)qrow * D + 16 * kk + 8 * h) ^ flip;
       qf[kk] = __builtin_bit_cast(bf16x8, x);
     }
   }
@@ -294,7 +315,7 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
   auto issue = [&](u32x4* dst, const uint16_t* src, const uint32_t (&off)[NLD], int kv0)
       __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(N - kv0) * RB), kRsrcWord3);
+        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(NK - kv0) * RB), kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) lds_load16(r, dst + (wave * NLD + i) * 64, off[i]);
   };
@@ -345,13 +366,14 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // ---- pieces of the softmax -------------------------------------------
-  // mask keys past N and, under the causal mask, after the query (only on the
-  // tiles that have such keys).  Element (kb, i) holds key kv0 + 32kb + 8h +
-  // kofs(i).
+  // mask keys past the workgroup's key range (past NK, or in the next
+  // workgroup's range) and, under the causal mask, after the query (only on
+  // the tiles that have such keys).  Element (kb, i) of tile j holds key
+  // j*BN + 32kb + 8h + kofs(i).
   auto mask = [&](f32x16 (&s)[NKB], int j) __attribute__((always_inline)) {
     const int kv0 = j * BN;
-    if (kv0 + BN > N || (CAUSAL && kv0 + BN - 1 > wave_q0)) {
-      const int lim = (CAUSAL ? min(N - 1, qrow) : N - 1) - kv0 - 8 * h;
+    if (kv0 + BN > kv_lim || (CAUSAL && kv0 + BN - 1 > wave_q0 + OFF)) {
+      const int lim = (CAUSAL ? min(kv_lim - 1, qrow + OFF) : kv_lim - 1) - kv0 - 8 * h;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -483,14 +505,14 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
 
   // ---- prologue ------------------------------------------------------------
   __syncthreads();  // zeroed K tiles visible before any load lands
-  if (n_tiles > 0) {
-    issue(kA, Kg, koff, 0);
-    issue(vA, Vg, voff, 0);
+  if (n_loc > 0) {
+    issue(kA, Kg, koff, t_lo * BN);
+    issue(vA, Vg, voff, t_lo * BN);
   }
-  if (n_tiles > 1) issue(kB, Kg, koff, BN);
-  __syncthreads();  // K_0, K_1, V_0 in LDS
+  if (n_loc > 1) issue(kB, Kg, koff, (t_lo + 1) * BN);
+  __syncthreads();  // the first two K tiles and the first V tile in LDS
   if (n_vis > 0) {
-    // scores of tile 0 and their reference (the running sums are still zero)
+    // scores of the first tile and their reference (the running sums are still zero)
 #pragma unroll
     for (int k = 0; k < NSA; ++k) {
       const int kk = k / NKB, kb = k % NKB;
@@ -498,15 +520,16 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
       sA[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kfrag(kA, k)), qf[kk],
                                                        kk == 0 ? z : sA[kb], 0, 0, 0);
     }
-    mask(sA, 0);
+    mask(sA, t_lo);
 #pragma unroll
     for (int k = 0; k <= NKB; ++k) ref_slice(sA, k);
     pend = false;
   }
 
   // ---- main loop: iteration j consumes S_j (scores in sc) and V_j^T --------
-  // Buffers: K_{j+1} is in Kn, K_{j+2} goes to Kd (which held K_j), V_j is in
-  // Vc, V_{j+1} goes to Vd (which held V_{j-1}).
+  // j counts the workgroup's tiles from 0 (key tile t_lo + j).  Buffers:
+  // K_{j+1} is in Kn, K_{j+2} goes to Kd (which held K_j), V_j is in Vc, V_{j+1}
+  // goes to Vd (which held V_{j-1}).
   auto iteration = [&](int j, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], const u32x4* Kn, u32x4* Kd,
                        const u32x4* Vc, u32x4* Vd) __attribute__((always_inline)) {
     // Everyone is done with iteration j-1 and its tile loads have landed.  The
@@ -515,41 +538,103 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
     // (it keeps it only at the barrier inside the loop body).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < n_tiles) issue(Vd, Vg, voff, (j + 1) * BN);
-    if (j + 2 < n_tiles) issue(Kd, Kg, koff, (j + 2) * BN);
+    if (j + 1 < n_loc) issue(Vd, Vg, voff, (t_lo + j + 1) * BN);
+    if (j + 2 < n_loc) issue(Kd, Kg, koff, (t_lo + j + 2) * BN);
     if (j >= n_vis) return;  // nothing of this tile or later is visible to this wave
     // One code path for every iteration (a second one for the last tile costs
     // more registers than the chip has): after the last visible tile the
     // "next" scores are computed from whatever K buffer is there and then fully
-    // masked, which leaves the reference and the sums unchanged, and are never
-    // used.
+    // masked (they lie past the key range or after every query of the wave),
+    // which leaves the reference and the sums unchanged, and are never used.
     u32x4 vf[NSB];
     phase_a(sc, sn, Kn, Vc, vf);
     apply_rescale();
-    mask(sn, j + 1);
+    mask(sn, t_lo + j + 1);
     phase_b(sn, Vc, vf);
   };
-  for (int j = 0; j < n_tiles; j += 2) {
+  for (int j = 0; j < n_loc; j += 2) {
     iteration(j, sA, sB, kB, kA, vA, vB);
-    if (j + 1 < n_tiles) iteration(j + 1, sB, sA, kA, kB, vB, vA);
+    if (j + 1 < n_loc) iteration(j + 1, sB, sA, kA, kB, vB, vA);
   }
 
-  // epilogue: O = o / l, LSE = (m + log2 lx) ln 2
+  // epilogue: O = o / l, LSE = (m + log2 lx) ln 2.  A split row that sees no
+  // key of its range (l = 0) records LSE = -inf and O = 0.
   const float l_tot = pair_sum(l);
   const float lx_tot = pair_sum(lx);
-  const float inv = 1.0f / l_tot;
-  if (qrow < N) {
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qrow < NQ) {
+    const float lse_row = l_tot > 0.0f ? (m_ref + __log2f(lx_tot)) * kLn2 : neg_inf();
+    if constexpr (SPLIT) {
+      const size_t prow = ((size_t)split * a.n_bh + bh) * NQ + qrow;
+      float* __restrict__ Op = a.o_part + prow * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * db + 8 * g + 4 * h;
-        const u32x2 w = {pack_bf16(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
-                         pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-        *(u32x2*)(Og + (size_t)qrow * D + d) = w;
-      }
-    if (h == 0) a.lse[(size_t)bh * N + qrow] = (m_ref + __log2f(lx_tot)) * kLn2;
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * h;
+          const f32x4 w = {o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                           o[db][4 * g + 3] * inv};
+          *(f32x4*)(Op + d) = w;
+        }
+      if (h == 0) a.lse_part[prow] = lse_row;
+    } else {
+      uint16_t* __restrict__ Og = (uint16_t*)a.o + ((size_t)bh * NQ + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * h;
+          const u32x2 w = {pack_bf16(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
+                           pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+          *(u32x2*)(Og + d) = w;
+        }
+      if (h == 0) a.lse[(size_t)bh * NQ + qrow] = lse_row;
+    }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the key ranges of a split launch: for every (b, h, query row),
+//   lse = ln sum_s exp(lse_s),   o = sum_s exp(lse_s - lse) o_s,
+// the online-softmax update of "Flash Attention" (wiki.ai-engineering.at,
+// section "Lösung: Online Softmax") applied to the summaries of whole key
+// ranges, with the largest lse_s subtracted before exponentiating.  Ranges in
+// which a row sees no key (lse_s = -inf) add nothing.  Each group of D/8 lanes
+// handles one row, 8 output elements per lane; O is rounded to bf16 once.
+constexpr int kCombineThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void fa_combine_kernel(FwdArgs a) {
+  constexpr int TPR = D / 8;                       // lanes per row
+  constexpr int RPB = kCombineThreads / TPR;       // rows per workgroup
+  const int tid = threadIdx.x;
+  const long long row = (long long)blockIdx.x * RPB + tid / TPR;
+  const int d0 = (tid % TPR) * 8;
+  if (row >= (long long)a.n_bh * a.nq) return;
+  const size_t stride = (size_t)a.n_bh * a.nq;     // between key ranges, in rows
+  float m = neg_inf();
+  for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, a.lse_part[s * stride + row]);
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  float tot = 0.0f;
+  constexpr float kLog2e = 1.44269504088896340736f;
+  for (int s = 0; s < a.n_split; ++s) {
+    const float ls = a.lse_part[s * stride + row];
+    if (ls == neg_inf()) continue;
+    const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
+    tot += w;
+    const float* __restrict__ op = a.o_part + (s * stride + row) * D + d0;
+    const f32x4 x0 = *(const f32x4*)op, x1 = *(const f32x4*)(op + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = __builtin_fmaf(w, x0[e], acc[e]);
+      acc[4 + e] = __builtin_fmaf(w, x1[e], acc[4 + e]);
+    }
+  }
+  const float inv = 1.0f / tot;
+  const u32x4 w = {pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv),
+                   pack_bf16(acc[4] * inv, acc[5] * inv), pack_bf16(acc[6] * inv, acc[7] * inv)};
+  *(u32x4*)((uint16_t*)a.o + row * D + d0) = w;
+  if (d0 == 0) a.lse[row] = m + __logf(tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -573,7 +658,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fa_fwd_f32_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
-  const int N = a.n;
+  const int N = a.nq;  // the fp32 path has as many queries as keys
 
   const int t = xcd_remap(blockIdx.x, a.n_blocks);
   const int bh = t / a.n_qblk;

@@ -46,6 +46,11 @@ class Workload:
     dtype: str  # "f32" or "bf16"
     causal: bool
     variant: int = PLAIN
+    NQ: int = 0  # query rows per head; 0: as many as keys (N)
+
+    @property
+    def nq(self) -> int:
+        return self.NQ if self.NQ > 0 else self.N
 
     @property
     def scale(self) -> float:
@@ -53,13 +58,28 @@ class Workload:
 
     @property
     def flops(self) -> float:
-        """Metric FLOPs of one forward: 4*B*H*N^2*D, halved when causal."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.D
-        return f / 2.0 if self.causal else f
+        """Metric FLOPs of one forward: 4*B*H*D times the (query, key) pairs,
+        N^2 (halved when causal) with as many queries as keys; with fewer
+        queries, Nq*N, or under the causal mask Nq*(N - Nq) + Nq^2/2."""
+        nq, nk = self.nq, self.N
+        if nq == nk:
+            pairs = nk * nk / (2.0 if self.causal else 1.0)
+        else:
+            pairs = nq * (nk - nq) + nq * nq / 2.0 if self.causal else float(nq * nk)
+        return 4.0 * self.B * self.H * self.D * pairs
+
+    @property
+    def kv_bytes(self) -> float:
+        """Bytes of K and V (the stream a decode step is bound by)."""
+        return 2.0 * self.B * self.H * self.N * self.D * (2 if self.dtype == "bf16" else 4)
+
+    def rows(self, t: int) -> int:
+        """Rows of tensor t in one head: nq for Q, N for K and V."""
+        return self.nq if t == T_Q else self.N
 
     def with_variant(self, variant: int) -> "Workload":
         return Workload(self.name + ("_peaked" if variant == PEAKED else ""), self.seed_id,
-                        self.B, self.H, self.N, self.D, self.dtype, self.causal, variant)
+                        self.B, self.H, self.N, self.D, self.dtype, self.causal, variant, self.NQ)
 
 
 # The five workloads attention is checked and measured on.
@@ -75,9 +95,16 @@ CAUSAL_LONG = Workload("bf16_causal_b1_h8_n131072_d128", 5, 1, 8, 131072, 128, "
 ALL_WORKLOADS = (FP32_SMALL, BF16_N4096) + CAUSAL_SWEEP + tuple(
     w.with_variant(PEAKED) for w in CAUSAL_SWEEP) + (CAUSAL_PREFILL, CAUSAL_LONG)
 
+# Workloads of the split-key path (queries fewer than keys): one new token per
+# head against a kept KV cache, and a 512-token chunk of a prompt whose first
+# 7680 tokens are already in the cache.
+SPLIT_DECODE = Workload("bf16_decode_b4_h32_nq1_nk16384_d128", 40, 4, 32, 16384, 128, "bf16", True, NQ=1)
+SPLIT_CHUNK = Workload("bf16_chunk_b1_h32_nq512_nk8192_d128", 41, 1, 32, 8192, 128, "bf16", True, NQ=512)
+SPLIT_WORKLOADS = (SPLIT_DECODE, SPLIT_CHUNK)
+
 
 def workload_by_name(name: str) -> Workload:
-    for w in ALL_WORKLOADS:
+    for w in ALL_WORKLOADS + SPLIT_WORKLOADS:
         if w.name == name:
             return w
     raise KeyError(name)
@@ -116,8 +143,9 @@ def _stream(seed_id: int, variant: int, b: int, h: int, t: int) -> np.random.Gen
 
 
 def head_tensor(w: Workload, b: int, h: int, t: int) -> np.ndarray:
-    """One [N, D] slice of tensor t (T_Q/T_K/T_V) as float32 values of w.dtype."""
-    x = _stream(w.seed_id, w.variant, b, h, t).standard_normal((w.N, w.D), dtype=np.float32)
+    """One [rows, D] slice of tensor t (T_Q/T_K/T_V) as float32 values of w.dtype
+    (rows = nq for Q, N for K and V)."""
+    x = _stream(w.seed_id, w.variant, b, h, t).standard_normal((w.rows(t), w.D), dtype=np.float32)
     if w.variant == PEAKED and t in (T_Q, T_K):
         x *= np.float32(PEAK_FACTOR)
     if w.dtype == "bf16":
@@ -126,7 +154,7 @@ def head_tensor(w: Workload, b: int, h: int, t: int) -> np.ndarray:
 
 
 def head_qkv(w: Workload, b: int, h: int):
-    """(q, k, v) for one (b, h): float32 arrays [N, D] holding exactly the kernel's inputs."""
+    """(q, k, v) for one (b, h): float32 arrays [rows, D] holding exactly the kernel's inputs."""
     return tuple(head_tensor(w, b, h, t) for t in (T_Q, T_K, T_V))
 
 
@@ -134,10 +162,10 @@ def _fill_one(args):
     w, b, h, t, path, offset = args
     x = head_tensor(w, b, h, t)
     if w.dtype == "bf16":
-        arr = np.memmap(path, dtype=np.uint16, mode="r+", offset=offset, shape=(w.N, w.D))
+        arr = np.memmap(path, dtype=np.uint16, mode="r+", offset=offset, shape=(w.rows(t), w.D))
         arr[:] = bf16_bits(x)
     else:
-        arr = np.memmap(path, dtype=np.float32, mode="r+", offset=offset, shape=(w.N, w.D))
+        arr = np.memmap(path, dtype=np.float32, mode="r+", offset=offset, shape=(w.rows(t), w.D))
         arr[:] = x
     arr.flush()
     del arr
@@ -145,14 +173,14 @@ def _fill_one(args):
 
 
 def full_tensor(w: Workload, t: int, workers: int | None = None) -> np.ndarray:
-    """The whole [B, H, N, D] tensor t, as raw element bits (uint16 for bf16, float32 for f32).
+    """The whole [B, H, rows, D] tensor t, as raw element bits (uint16 for bf16, float32 for f32).
 
     Slices are drawn in parallel worker processes when the tensor is large.
     """
     dt = np.uint16 if w.dtype == "bf16" else np.float32
-    shape = (w.B, w.H, w.N, w.D)
+    shape = (w.B, w.H, w.rows(t), w.D)
     n_slices = w.B * w.H
-    slice_elems = w.N * w.D
+    slice_elems = w.rows(t) * w.D
     if workers is None:
         workers = min(16, len(os.sched_getaffinity(0)))
     if n_slices * slice_elems < (1 << 22) or workers <= 1:
@@ -184,9 +212,9 @@ def sample_heads(w: Workload, count: int) -> list[tuple[int, int]]:
 
 
 def sample_rows(w: Workload, h: int, count: int, edges: bool = True) -> np.ndarray:
-    """Seeded query rows of head h, without replacement, plus rows 0 and N-1, sorted."""
+    """Seeded query rows of head h, without replacement, plus the first and last row, sorted."""
     g = _stream(w.seed_id, 0, 999, h, 1)
-    rows = set(int(i) for i in g.choice(w.N, size=min(count, w.N), replace=False))
+    rows = set(int(i) for i in g.choice(w.nq, size=min(count, w.nq), replace=False))
     if edges:
-        rows |= {0, w.N - 1}
+        rows |= {0, w.nq - 1}
     return np.array(sorted(rows), dtype=np.int64)

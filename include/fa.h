@@ -18,8 +18,12 @@
  * точно?").
  *
  * Causal mask: key j is visible to query i iff j <= i (queries and keys share
- * one sequence of length N).  The pages name masking without defining it; this
- * is the reading the library implements.
+ * one sequence of length N).  With fewer queries (Nq) than keys (Nk), in
+ * fa_fwd_split, the queries are the last Nq positions of the sequence: key j
+ * is visible to query i iff j <= i + Nk - Nq, as when new tokens attend to a
+ * kept KV cache (ZimaSpace, section "Weniger IO bedeutet nicht, dass der
+ * KV-Cache entfällt").  The pages name masking without defining it; these are
+ * the readings the library implements.
  *
  * LSE is not on the pages: it is the per-row statistic a backward pass needs,
  * returned in natural-log units for every row.
@@ -38,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 /* Identical to hipStream_t.  NULL means the device's null stream. */
 typedef struct ihipStream_t* fa_stream_t;
@@ -59,7 +63,8 @@ typedef enum fa_status {
   FA_ERR_ALIASING = 6,     /* o or lse overlaps q, k, v or each other                 */
   FA_ERR_UNSUPPORTED = 7,  /* valid but not built: D not 64/128, N*D >= 2^31, more   */
                            /* than 2^31-1 workgroups, or the device is not gfx950     */
-  FA_ERR_HIP = 8           /* a HIP runtime call failed (no device, launch failure)   */
+  FA_ERR_HIP = 8,          /* a HIP runtime call failed (no device, launch failure)   */
+  FA_ERR_WORKSPACE = 9     /* fa_fwd_split: workspace_bytes below what the call needs */
 } fa_status;
 
 /* Byte sizes of every buffer of one call. */
@@ -113,6 +118,65 @@ fa_status fa_fwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal,
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
                  fa_dtype dtype, fa_stream_t stream);
+
+/* fa_fwd_split: let the library choose the number of key ranges. */
+#define FA_SPLIT_AUTO 0
+/* Largest number of key ranges fa_fwd_split accepts. */
+#define FA_SPLIT_MAX 256
+
+/*
+ * fa_fwd_split_query - buffer sizes of an fa_fwd_split call, and the number of
+ * key ranges it will use.
+ *
+ * Pure host function (no device).  q and o are [B, H, Nq, D], k and v
+ * [B, H, Nk, D], lse [B, H, Nq]; workspace_bytes is what the call needs beyond
+ * them: 0 for one range, else n_splits * B * H * Nq * (D + 1) * 4 (a float32
+ * output row and log-sum-exp per query row and range).  *splits_out (if not
+ * NULL) receives the number of ranges: n_splits itself, or for FA_SPLIT_AUTO
+ * the library's choice, which depends only on the arguments: enough ranges
+ * for about 512 workgroups, but at least 8 key tiles of 64 per range, at most
+ * Nk / (4 Nq) ranges (partial results within a quarter of the K/V bytes) and at
+ * most 64; so one range unless the queries are few against many keys.  *out and *splits_out are written only on FA_OK.
+ * Returns FA_OK, FA_ERR_BAD_SHAPE (a size <= 0, Nq > Nk with
+ * causal, n_splits outside 0..FA_SPLIT_MAX, overflow), FA_ERR_BAD_DTYPE,
+ * FA_ERR_NULL_POINTER (out NULL) or FA_ERR_UNSUPPORTED (not bf16, D not in
+ * {64, 128}, Nq*D or Nk*D >= 2^31, more than 2^31-1 workgroups).
+ */
+fa_status fa_fwd_split_query(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
+                             int n_splits, fa_dtype dtype, fa_sizes* out, int* splits_out);
+
+/*
+ * fa_fwd_split - exact attention forward with the keys of every query block
+ * divided into contiguous ranges processed by separate workgroups, then merged.
+ *
+ * Fills the device when B*H*ceil(Nq/128) alone gives few workgroups (short
+ * sequences, one or a few new tokens against a long KV cache).  Each range
+ * yields, per query row, its normalised output and log-sum-exp; a second
+ * kernel on the same stream merges them, lse = ln sum_s exp(lse_s),
+ * o = sum_s exp(lse_s - lse) o_s: the online-softmax update of "Flash
+ * Attention" (wiki.ai-engineering.at, section "Lösung: Online Softmax")
+ * applied to whole ranges.  The pages name this use ("Flash-Decoding", same
+ * page, section "Ergebnisse") without giving its steps.
+ *
+ * q, o      : [B, H, Nq, D] bfloat16 contiguous (o written).
+ * k, v      : [B, H, Nk, D] bfloat16 contiguous; q, k, v may alias.
+ * lse       : float32 [B, H, Nq], written.
+ * workspace : device scratch of workspace_bytes >= the size fa_fwd_split_query
+ *             reports (may be NULL when that is 0), 16-byte aligned, not
+ *             overlapping any other buffer; owned by the caller, contents on
+ *             entry ignored, clobbered.  Calls that share a workspace must be
+ *             ordered (same stream or synchronised).
+ * causal    : as in fa_fwd, with the queries as the last Nq positions (Nq <= Nk).
+ * n_splits  : FA_SPLIT_AUTO or 1 .. FA_SPLIT_MAX.  With one range no workspace
+ *             is used and a single kernel writes o and lse.
+ *
+ * Validation and asynchrony as in fa_fwd; FA_ERR_WORKSPACE when workspace_bytes
+ * is too small.  bfloat16 only.  Allocates nothing.
+ */
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
+                       int64_t Nk, int64_t D, int causal, float scale, int n_splits, fa_dtype dtype,
+                       fa_stream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);

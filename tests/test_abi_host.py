@@ -45,8 +45,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert fa.fa_abi_version() == 1
-    for st in range(9):
+    assert fa.fa_abi_version() == 2
+    for st in range(10):
         s = fa.fa_status_str(st)
         assert s.startswith("FA_")
     assert fa.fa_status_str(99) == "unknown fa_status"
@@ -143,5 +143,80 @@ def test_every_kernel_stub_is_defined():
     out = subprocess.run(["nm", "-D", fab.LIB_PATH], capture_output=True, text=True).stdout
     undefined = [l for l in out.splitlines() if " U " in l and "_ZN2fa" in l]
     assert undefined == []
-    kernels = set(re.findall(r"(_ZN2fa\d+fa_fwd_\w+_kernelI\w+)", out))
-    assert len(kernels) == 8, kernels
+    kernels = set(re.findall(r"(_ZN2fa\d+fa_\w+_kernelI\w+)", out))
+    # bf16: D x causal x split; fp32: D x causal; merge: D
+    assert len(kernels) == 8 + 4 + 2, kernels
+
+
+# ---------------------------------------------------------------- fa_fwd_split
+def test_split_query_sizes_and_ranges():
+    st, sz, s = fa.fa_fwd_split_query(4, 32, 1, 16384, 128, 1, fa.FA_SPLIT_AUTO, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK
+    assert sz.q_bytes == sz.o_bytes == 4 * 32 * 1 * 128 * 2
+    assert sz.k_bytes == sz.v_bytes == 4 * 32 * 16384 * 128 * 2
+    assert sz.lse_bytes == 4 * 32 * 4
+    # 128 query blocks: 4 ranges give 512 workgroups
+    assert s == 4 and sz.workspace_bytes == 4 * 4 * 32 * 1 * (128 + 1) * 4
+    # one range: no workspace
+    st, sz, s = fa.fa_fwd_split_query(2, 32, 4096, 4096, 128, 0, 1, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK and s == 1 and sz.workspace_bytes == 0
+    # enough query blocks already: the automatic choice is one range
+    st, sz, s = fa.fa_fwd_split_query(2, 32, 4096, 4096, 128, 0, fa.FA_SPLIT_AUTO, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK and s == 1 and sz.workspace_bytes == 0
+    # caps: 8 key tiles per range ...
+    st, sz, s = fa.fa_fwd_split_query(1, 1, 16, 8192, 64, 1, fa.FA_SPLIT_AUTO, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK and s == 16
+    st, sz, s = fa.fa_fwd_split_query(1, 1, 16, 300, 64, 1, fa.FA_SPLIT_AUTO, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK and s == 1
+    # ... partial results within a quarter of the K/V bytes ...
+    st, sz, s = fa.fa_fwd_split_query(1, 32, 512, 8192, 128, 1, fa.FA_SPLIT_AUTO, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK and s == 4
+    # ... so square shapes stay on one range
+    st, sz, s = fa.fa_fwd_split_query(1, 32, 512, 512, 128, 1, fa.FA_SPLIT_AUTO, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK and s == 1 and sz.workspace_bytes == 0
+    # an explicit count is used as given
+    st, sz, s = fa.fa_fwd_split_query(1, 2, 100, 900, 64, 0, 7, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK and s == 7 and sz.workspace_bytes == 7 * 2 * 100 * 65 * 4
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((1, 1, 10, 5, 64, 1, 0, fa.FA_DTYPE_BF16), fa.FA_ERR_BAD_SHAPE),     # causal with Nq > Nk
+    ((1, 1, 10, 5, 64, 0, 0, fa.FA_DTYPE_BF16), fa.FA_OK),                # fine without the mask
+    ((1, 1, 0, 5, 64, 0, 0, fa.FA_DTYPE_BF16), fa.FA_ERR_BAD_SHAPE),
+    ((1, 1, 4, 64, 64, 0, -1, fa.FA_DTYPE_BF16), fa.FA_ERR_BAD_SHAPE),
+    ((1, 1, 4, 64, 64, 0, 257, fa.FA_DTYPE_BF16), fa.FA_ERR_BAD_SHAPE),
+    ((1, 1, 4, 64, 64, 0, 256, fa.FA_DTYPE_BF16), fa.FA_OK),
+    ((1, 1, 4, 64, 64, 0, 0, fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
+    ((1, 1, 4, 64, 96, 0, 0, fa.FA_DTYPE_BF16), fa.FA_ERR_UNSUPPORTED),
+    ((1, 1, 4, 64, 64, 0, 0, 3), fa.FA_ERR_BAD_DTYPE),
+])
+def test_split_query_validation(args, expect):
+    assert fa.fa_fwd_split_query(*args)[0] == expect
+
+
+def split_call(q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, lse=A + 4 * SZ, ws=A + 5 * SZ, ws_bytes=SZ,
+               B=1, H=2, Nq=10, Nk=300, D=64, causal=1, scale=0.125, n_splits=3, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_fwd_split(q, k, v, o, lse, ws, ws_bytes, B, H, Nq, Nk, D, causal, scale, n_splits, dtype, None)
+
+
+WS3 = 3 * 2 * 10 * 65 * 4  # workspace of the default split_call
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(ws=0), fa.FA_ERR_NULL_POINTER),
+    (dict(ws=0, n_splits=1), fa.FA_ERR_HIP),              # one range needs no workspace
+    (dict(ws_bytes=WS3 - 1), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=WS3), fa.FA_ERR_HIP),                  # exactly enough: valid
+    (dict(ws=A + 5 * SZ + 8), fa.FA_ERR_MISALIGNED),
+    (dict(ws=A + 2 * SZ), fa.FA_ERR_ALIASING),            # workspace on top of v
+    (dict(ws=A + 3 * SZ + 16), fa.FA_ERR_ALIASING),       # workspace inside o
+    (dict(Nq=301), fa.FA_ERR_BAD_SHAPE),                  # causal, more queries than keys
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE),
+    (dict(dtype=fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(o=A + SZ), fa.FA_ERR_ALIASING),
+    (dict(lse=0), fa.FA_ERR_NULL_POINTER),
+])
+def test_split_validation_before_any_device_call(kw, expect):
+    if expect == fa.FA_ERR_HIP and gpu_visible():
+        pytest.skip("valid arguments would launch on fake addresses when a GPU is visible")
+    assert split_call(**kw) == expect
