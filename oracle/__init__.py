@@ -5,6 +5,7 @@ benchmark's cpu_baseline leg may import it.  The HIP library never does, and
 this package imports nothing from the library (numpy only).
 """
 from .attention import attention_ref, attention_ref_bhnd, merge_ref
+from .backward import attention_bwd_ref
 from .tiled import tiled_ref
 
-__all__ = ["attention_ref", "attention_ref_bhnd", "merge_ref", "tiled_ref"]
+__all__ = ["attention_ref", "attention_ref_bhnd", "attention_bwd_ref", "merge_ref", "tiled_ref"]
