@@ -2,7 +2,7 @@
 """Benchmark of the exact-attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--split S] [--no-cpu-baseline] [--sweep]
+                    [--split S] [--backward] [--no-cpu-baseline] [--sweep]
 
 A step is one fa_fwd call (the whole hot path: one kernel) over the workload's
 synthetic inputs, already resident in device memory.  Prints ONE JSON line:
@@ -16,6 +16,12 @@ workload run with --split S (S key ranges; 0 = the library's choice), step
 through fa_fwd_split: the range kernel and the merge kernel, both inside the
 timed events.  Their roofline is the HBM one (GB/s of Q, K, V, O and LSE) when
 the workload's arithmetic intensity is below the machine balance.
+
+With --backward a step is one fa_bwd call (its two kernels: dq with Delta, then
+dk and dv) for a seeded upstream gradient, O and LSE having been computed by
+fa_fwd before the timed region.  FLOPs are those of the five products of the
+gradient, 10*B*H*N^2*D (halved when causal): 2.5 times the forward's, whatever
+the kernels recompute.
 """
 from __future__ import annotations
 
@@ -36,6 +42,7 @@ HEADLINE = "bf16_b2_h32_n4096_d128"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 KERNEL_SOURCES = ["exact_attention_65_amd/csrc/fa_fwd_kernel.hpp", "exact_attention_65_amd/csrc/fa_fwd.hip"]
+BWD_FLOP_FACTOR = 2.5  # five N x N x D products against the forward's two
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_bf16_d128_b2_h32_n4096.txt")
 
 
@@ -66,11 +73,12 @@ def read_traffic(workload: str):
         return None
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The fp64 oracle on whole (b, h) heads of the workload until the budget is spent."""
+def cpu_baseline(w, budget_s: float = 12.0, backward: bool = False):
+    """The fp64 oracle on whole (b, h) heads of the workload until the budget is spent
+    (the gradient oracle with --backward)."""
     import numpy as np
     import fa_inputs as fi
-    from oracle import attention_ref
+    from oracle import attention_bwd_ref, attention_ref
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
@@ -82,13 +90,17 @@ def cpu_baseline(w, budget_s: float = 12.0):
     t_total = 0.0
     for b, h in heads:
         q, k, v = fi.head_qkv(w, b, h)
+        do = fi.head_tensor(w, b, h, fi.T_DO) if backward else None
         t0 = time.perf_counter()
-        attention_ref(q, k, v, w.causal, w.scale)
+        if backward:
+            attention_bwd_ref(q, k, v, do, w.causal, w.scale)
+        else:
+            attention_ref(q, k, v, w.causal, w.scale)
         t_total += time.perf_counter() - t0
         done += 1
         if t_total >= budget_s:
             break
-    flops = w.flops / (w.B * w.H) * done
+    flops = w.flops / (w.B * w.H) * done * (BWD_FLOP_FACTOR if backward else 1.0)
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} of {len(heads)} (b,h) heads of {w.name}, every query row, numpy float64 "
                       f"({t_total:.2f} s)"}
@@ -102,6 +114,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--split", type=int, default=None,
                     help="run through fa_fwd_split with this many key ranges (0 = library's choice)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time fa_bwd (the gradients) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="one line per workload instead of the headline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -134,6 +148,10 @@ def main():
     for name in names:
         w = fi.workload_by_name(name)
         split = args.split if args.split is not None else (fa.FA_SPLIT_AUTO if w.NQ > 0 else None)
+        if args.backward:
+            split = None
+            if w.dtype != "bf16" or w.NQ > 0:
+                continue
         if split is not None and w.dtype != "bf16":
             continue
         dt = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32
@@ -156,8 +174,24 @@ def main():
                 raise fa.FaError(st)
             ws = torch.empty(max(1, sz.workspace_bytes), dtype=torch.uint8, device=q.device)
 
+        if args.backward:
+            bits = fi.full_tensor(w, fi.T_DO)
+            do = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+            del bits
+            fa.attention_forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            grads = [torch.empty_like(q) for _ in range(3)]
+            st, sz = fa.fa_bwd_query(w.B, w.H, w.N, w.D, w.causal, dt)
+            if st != fa.FA_OK:
+                raise fa.FaError(st)
+            ws = torch.empty(sz.workspace_bytes, dtype=torch.uint8, device=q.device)
+        flops = w.flops * (BWD_FLOP_FACTOR if args.backward else 1.0)
+
         def step():
-            if split is None:
+            if args.backward:
+                st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                               lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+                               ws.data_ptr(), ws.numel(), w.B, w.H, w.N, w.D, w.causal, w.scale, dt, sp)
+            elif split is None:
                 st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                w.B, w.H, w.N, w.D, w.causal, w.scale, dt, sp)
             else:
@@ -196,12 +230,12 @@ def main():
         launch_ms = np.array([a.elapsed_time(b) for a, b in evs])
         kernel_ms = float(launch_ms.mean())
 
-        tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+        tflops = flops / (ms_per_step * 1e-3) / 1e12
         peak = PEAK_TFLOPS[w.dtype]
-        achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
         elt = 2 if w.dtype == "bf16" else 4
         alg_bytes = w.kv_bytes + 2.0 * w.B * w.H * w.nq * w.D * elt + 4.0 * w.B * w.H * w.nq
-        hbm_bound = w.flops / alg_bytes < peak / PEAK_HBM_GBS * 1e3  # intensity below machine balance
+        hbm_bound = flops / alg_bytes < peak / PEAK_HBM_GBS * 1e3  # intensity below machine balance
         if hbm_bound:
             roofline = {"bound": "hbm", "achieved": round(alg_bytes / (kernel_ms * 1e-3) / 1e9, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -209,9 +243,10 @@ def main():
         else:
             roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                         "frac": round(achieved / peak, 4),
-                        "traffic": read_traffic(w.name) if split is None else None}
+                        "traffic": read_traffic(w.name) if split is None and not args.backward else None}
         rec = {
-            "metric": METRIC if w.name == HEADLINE else
+            "metric": "bwd attention TFLOP/s (10*D per visible (query, key) pair) of workload " + w.name
+            if args.backward else METRIC if w.name == HEADLINE else
             "fwd attention TFLOP/s (4*D per visible (query, key) pair) of workload " + w.name,
             "value": round(tflops, 2),
             "unit": "TFLOP/s",
@@ -228,7 +263,8 @@ def main():
                     + (" rounded to bf16" if w.dtype == "bf16" else ""),
             "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "Nq": w.nq, "D": w.D,
                        "causal": w.causal, "scale": w.scale, "parallelism": "single GPU",
-                       "entry_point": "fa_fwd" if split is None else f"fa_fwd_split ({n_ranges} key ranges)",
+                       "entry_point": "fa_bwd (dq kernel + dk/dv kernel)" if args.backward else
+                       "fa_fwd" if split is None else f"fa_fwd_split ({n_ranges} key ranges)",
                        "pct_of_peak": round(100 * tflops / peak, 2),
                        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
                        "launch_ms_min": round(float(launch_ms.min()), 5),
@@ -238,7 +274,7 @@ def main():
         if not args.no_cpu_baseline and not args.sweep:
             del q, k, v, o, lse
             torch.cuda.empty_cache()
-            rec["cpu_baseline"] = cpu_baseline(w)
+            rec["cpu_baseline"] = cpu_baseline(w, backward=args.backward)
         print(json.dumps(rec), flush=True)
 
 

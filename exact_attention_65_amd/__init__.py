@@ -1,11 +1,11 @@
-"""Python binding of the MI355X exact-attention forward library (include/fa.h).
+"""Python binding of the MI355X exact-attention library (include/fa.h).
 
 Argument marshalling only: every step of the attention runs in the HIP
 kernels of libfa_mi355x.so.  The names mirror the C ABI (fa_fwd, fa_fwd_query,
-fa_fwd_split, fa_fwd_split_query, fa_status_str, fa_abi_version);
-``attention_forward`` and ``attention_forward_split`` are the torch-facing
-helpers that allocate O, LSE (and the split workspace) with torch and pass
-torch's current stream.
+fa_fwd_split, fa_fwd_split_query, fa_bwd, fa_bwd_query, fa_status_str,
+fa_abi_version); ``attention_forward``, ``attention_forward_split`` and
+``attention_backward`` are the torch-facing helpers that allocate outputs (and
+workspaces) with torch and pass torch's current stream.
 
 The library is loaded on first use; if it has not been built
 (``python -m exact_attention_65_amd.build``) that use raises ImportError.
@@ -36,8 +36,8 @@ FA_ERR_WORKSPACE = 9
 FA_SPLIT_AUTO = 0
 FA_SPLIT_MAX = 256
 
-EXPORTED = ("fa_fwd", "fa_fwd_query", "fa_fwd_split", "fa_fwd_split_query", "fa_status_str",
-            "fa_abi_version")
+EXPORTED = ("fa_fwd", "fa_fwd_query", "fa_fwd_split", "fa_fwd_split_query", "fa_bwd", "fa_bwd_query",
+            "fa_status_str", "fa_abi_version")
 
 
 class FaSizes(ctypes.Structure):
@@ -67,6 +67,11 @@ def _load():
     lib.fa_fwd_split_query.restype = ctypes.c_int
     lib.fa_fwd_split_query.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.POINTER(FaSizes), ctypes.POINTER(ctypes.c_int)]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64,
+                           ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+    lib.fa_bwd_query.restype = ctypes.c_int
+    lib.fa_bwd_query.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(FaSizes)]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_abi_version.restype = ctypes.c_int
@@ -112,6 +117,20 @@ def fa_fwd_split_query(B, H, Nq, Nk, D, causal, n_splits, dtype):
     st = lib().fa_fwd_split_query(B, H, Nq, Nk, D, int(causal), int(n_splits), int(dtype), ctypes.byref(sz),
                                   ctypes.byref(splits))
     return st, sz, splits.value
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, D, causal, scale, dtype,
+           stream) -> int:
+    """Raw C call: pointers as integers (device addresses), returns the fa_status."""
+    return lib().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, D, int(causal),
+                        float(scale), int(dtype), stream)
+
+
+def fa_bwd_query(B, H, N, D, causal, dtype):
+    """Returns (status, FaSizes)."""
+    sz = FaSizes()
+    st = lib().fa_bwd_query(B, H, N, D, int(causal), int(dtype), ctypes.byref(sz))
+    return st, sz
 
 
 def fa_status_str(status: int) -> str:
@@ -195,3 +214,43 @@ def attention_forward_split(q, k, v, causal: bool = False, scale: float | None =
     if st != FA_OK:
         raise FaError(st)
     return out, lse
+
+
+def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+                       dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dq, dk, dv of attention_forward's o for the upstream gradient dout.
+
+    q, k, v, o, dout: contiguous bf16 GPU tensors [B, H, N, D]; o and lse as
+    attention_forward returned them for the same q, k, v, causal and scale.
+    Allocates the gradients (and the workspace, unless a uint8 GPU tensor is
+    given) with torch.  Launches on ``stream`` (default: torch's current
+    stream); no synchronisation.
+    """
+    import torch
+    if q.dtype != torch.bfloat16:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for x in (q, k, v, o, dout):
+        if x.dtype != q.dtype or x.shape != q.shape or not x.is_cuda or not x.is_contiguous():
+            raise ValueError("q, k, v, o, dout must be contiguous GPU tensors of one shape and dtype")
+    B, H, N, D = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st, sz = fa_bwd_query(B, H, N, D, causal, FA_DTYPE_BF16)
+    if st != FA_OK:
+        raise FaError(st)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(sz.workspace_bytes, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), B, H, N, D, causal, scale, FA_DTYPE_BF16,
+                stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return dq, dk, dv

@@ -1,0 +1,67 @@
+// Host launcher and C entry point of the attention backward (see include/fa.h).
+//
+// Two launches on the caller's stream: fa_bwd_dq_kernel (one workgroup per 128
+// query rows: dq, and Delta = rowsum(dO O) into the workspace), then
+// fa_bwd_dkdv_kernel (one workgroup per 128 keys: dk, dv), which reads Delta.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+
+#include "fa.h"
+#include "fa_bwd_kernel.hpp"
+#include "fa_check.h"
+#include "fa_device.h"
+
+namespace fa {
+namespace {
+
+template <typename Kern>
+hipError_t launch(Kern kern, const BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(kern, dim3(a.n_blocks), dim3(kBwdThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(int D, bool causal, BwdArgs a, float scale, hipStream_t s) {
+  // dq kernel: Q's signs carry the sign of scale
+  a.flip = std::signbit(scale) && scale != 0.0f ? 0x80008000u : 0u;
+  hipError_t e;
+  if (D == 128) e = causal ? launch(fa_bwd_dq_kernel<128, true>, a, s) : launch(fa_bwd_dq_kernel<128, false>, a, s);
+  else e = causal ? launch(fa_bwd_dq_kernel<64, true>, a, s) : launch(fa_bwd_dq_kernel<64, false>, a, s);
+  if (e != hipSuccess) return e;
+  // dkdv kernel: K's signs carry it
+  if (D == 128) return causal ? launch(fa_bwd_dkdv_kernel<128, true>, a, s) : launch(fa_bwd_dkdv_kernel<128, false>, a, s);
+  return causal ? launch(fa_bwd_dkdv_kernel<64, true>, a, s) : launch(fa_bwd_dkdv_kernel<64, false>, a, s);
+}
+
+}  // namespace
+}  // namespace fa
+
+extern "C" __attribute__((visibility("default"))) fa_status fa_bwd(
+    const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+    void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t D,
+    int causal, float scale, fa_dtype dtype, fa_stream_t stream) {
+  fa_status st = fa::check_bwd_call(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, D,
+                                    scale, (int)dtype);
+  if (st != FA_OK) return st;
+  if ((st = fa::device_check()) != FA_OK) return st;
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float*)workspace;
+  a.n = (int)N;
+  a.n_blk = (int)((N + fa::kBwdRows - 1) / fa::kBwdRows);
+  a.n_blocks = (int)(B * H * a.n_blk);
+  const float c = std::fabs(scale) * 1.44269504088896340736f;
+  a.c = c < FLT_MIN ? FLT_MIN : c;
+  a.scale = scale;
+  a.flip = 0u;
+  return fa::launch_bwd((int)D, causal != 0, a, scale, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

@@ -1,0 +1,429 @@
+// Gradients of the exact attention forward for CDNA4 (gfx950), bf16 inputs.
+//
+// The pages say only that a second pass computes the gradients over the same
+// chunks without storing the score matrix ("Flash Attention: ускорить
+// attention в 6 раз без потери точности", johe.ru, section "Стадии
+// вычисления").  With the forward's log-sum-exp saved, every weight is
+// recomputed exactly as P = exp(scale q.k - LSE), and for the upstream dO:
+//   Delta_i = sum_d dO_id O_id,  dP = dO V^T,  dS = P (dP - Delta),
+//   dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q.
+// Two kernels, neither using atomics:
+//   fa_bwd_dq_kernel    one workgroup per 128 query rows, K and V tiles streamed
+//                       (the forward's loop): S^T = K Q^T, dP^T = V dO^T, then
+//                       dQ^T += K^T dS^T; it also writes Delta for its rows;
+//   fa_bwd_dkdv_kernel  one workgroup per 128 keys, Q and dO tiles streamed:
+//                       S = Q K^T, dP = dO V^T, then dV^T += dO^T P and
+//                       dK^T += Q^T dS.
+// Every contraction runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulators; P
+// and dS are rounded to bf16 as MFMA operands, outputs to bf16 once.
+#pragma once
+
+#include "fa_fwd_kernel.hpp"
+
+namespace fa {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // [B*H*N], natural log, from the forward
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;      // [B*H*N] workspace: sum_d dO O per row
+  int n;             // sequence length N
+  int n_blk;         // 128-row blocks per (b, h)
+  int n_blocks;      // workgroups in the grid: B * H * n_blk
+  float c;           // |scale| * log2(e), at least FLT_MIN
+  float scale;       // the signed scale, applied to dQ and dK at the end
+  uint32_t flip;     // XOR on the register-held Q (dq kernel) or K (dkdv kernel) bits: sign of scale
+};
+
+constexpr int kBwdThreads = 256;
+constexpr int kBwdRows = 128;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+namespace bwd {
+
+// Byte offset of 16-byte chunk `chunk` of tile row `row` (rows of D bf16,
+// chunks XOR-swizzled by kswz as in the forward's K tiles).
+template <int D>
+__device__ __forceinline__ uint32_t chunk_addr(int row, int chunk) {
+  return (uint32_t)(row * D * 2 + ((chunk ^ kswz<D>(row)) * 16));
+}
+
+// A-operand rows of a 32-row MFMA block from a tile: row 32kb + swap23(c32),
+// columns 16kk + 8h .. +7 (one 16-byte chunk).
+template <int D>
+__device__ __forceinline__ u32x4 row_frag(const u32x4* t, int kb, int kk, int c32, int h) {
+  const int row = 32 * kb + swap23(c32);
+  return *(const u32x4*)((const char*)t + chunk_addr<D>(row, 2 * kk + h));
+}
+
+// A-operand of the transposed tile (columns of the tile as MFMA rows): 32
+// columns 32db .. 32db+31, 16 rows 16cc .. 16cc+15, by two transposing reads
+// per lane; the lane layout is the forward's V^T read, here through kswz.
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag(const u32x4* t, int db, int cc, int lane) {
+  const int g = lane >> 4, i16 = lane & 15;
+  const int hh = g >> 1, gg = g & 1, r = i16 >> 2, q = i16 & 3;
+  const int chunk = 4 * db + 2 * gg + (q >> 1);
+  const int row = 16 * cc + 8 * hh + r;
+  const char* base = (const char*)t + (q & 1) * 8;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + chunk_addr<D>(row, chunk)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + chunk_addr<D>(row + 4, chunk)));
+  return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Row of the operand held in registers: [row][16kk + 8h .. +7] as MFMA B
+// fragments, signs flipped by `flip`, zero for rows past N.
+template <int NKK>
+__device__ __forceinline__ void load_row(bf16x8 (&f)[NKK], const uint16_t* g, int row, int N, int D, int h,
+                                         uint32_t flip) {
+  const u32x4 fl = {flip, flip, flip, flip};
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (row < N) x = *(const u32x4*)(g + (size_t)row * D + 16 * kk + 8 * h) ^ fl;
+    f[kk] = __builtin_bit_cast(bf16x8, x);
+  }
+}
+
+// Pack 8 consecutive fp32 values of an accumulator into one bf16x8 operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
+  // scalars first: this compiler miscompiles __builtin_bit_cast of a vector element
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16(s[base + 2 * e], s[base + 2 * e + 1]);
+  const u32x4 x = {w[0], w[1], w[2], w[3]};
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+// Store a [D x 32] MFMA accumulator (rows d, this lane's column = one row of
+// the output) as bf16 after multiplying by mul.
+template <int NDB>
+__device__ __forceinline__ void store_rows(uint16_t* out_row, const f32x16 (&acc)[NDB], int h, float mul) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * h;
+      const u32x2 w = {pack_bf16(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul),
+                       pack_bf16(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+      *(u32x2*)(out_row + d) = w;
+    }
+}
+
+}  // namespace bwd
+
+// ---------------------------------------------------------------------------
+// dQ (and Delta): 4 waves x 32 query rows; 64-key K and V tiles streamed
+// through double-buffered LDS by buffer-to-LDS loads, one barrier per tile.
+// Per tile and wave: 16 MFMAs S^T = K Q^T (keys on rows, this lane's query on
+// the columns: the forward's orientation), 16 MFMAs dP^T = V dO^T, the
+// elementwise dS^T = P^T (dP^T - Delta), and 16 MFMAs dQ^T += K^T dS^T with
+// K^T read transposed from the same tile.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
+  constexpr int BN = 64, RB = D * 2, CPR = D / 8, RPB = 64 / CPR, TILE16 = BN * CPR;
+  constexpr int NLD = TILE16 / 64 / 4, NKB = BN / 32, NDB = D / 32, NKK = D / 16, NCC = BN / 16;
+  __shared__ u32x4 kA[TILE16], kB[TILE16], vA[TILE16], vB[TILE16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, c32 = lane & 31;
+  const int N = a.n;
+  const int t = xcd_remap(blockIdx.x, a.n_blocks);
+  const int bh = t / a.n_blk;
+  int qb = t - bh * a.n_blk;
+  if (CAUSAL) qb = a.n_blk - 1 - qb;  // longest query blocks first
+  const int q0 = qb * kBwdRows;
+  const size_t head = (size_t)bh * N * D;
+  const uint16_t* Qg = (const uint16_t*)a.q + head;
+  const uint16_t* Kg = (const uint16_t*)a.k + head;
+  const uint16_t* Vg = (const uint16_t*)a.v + head;
+  const uint16_t* Og = (const uint16_t*)a.o + head;
+  const uint16_t* dOg = (const uint16_t*)a.dout + head;
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBwdRows) : N;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+  const int qrow = q0 + wave * 32 + c32;
+  const int wave_q0 = q0 + wave * 32;
+  const int n_vis = wave_q0 >= N ? 0 : CAUSAL ? min(n_tiles, (wave_q0 + 31) / BN + 1) : n_tiles;
+
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < TILE16; i += kBwdThreads) kA[i] = kB[i] = vA[i] = vB[i] = z;
+  }
+
+  // this lane's query row: Q (signs flipped for a negative scale) and dO as MFMA
+  // B fragments; Delta = sum_d dO O (each half-wave holds half the d's)
+  bf16x8 qf[NKK], dof[NKK];
+  bwd::load_row(qf, Qg, qrow, N, D, h, a.flip);
+  bwd::load_row(dof, dOg, qrow, N, D, h, 0u);
+  float dsum = 0.0f;
+  {
+    bf16x8 of[NKK];
+    bwd::load_row(of, Og, qrow, N, D, h, 0u);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const u32x4 x = __builtin_bit_cast(u32x4, dof[kk]), y = __builtin_bit_cast(u32x4, of[kk]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t xe = x[e], ye = y[e];
+        dsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xe), __builtin_bit_cast(bf16x2, ye),
+                                               dsum, false);
+      }
+    }
+  }
+  const float delta = pair_sum(dsum);
+  if (qrow < N && h == 0) a.delta[(size_t)bh * N + qrow] = delta;
+  const float lse2 = qrow < N ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.0f;
+
+  uint32_t koff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int row = (wave * NLD + i) * RPB + lane / CPR;
+    koff[i] = row * RB + (((lane % CPR) ^ kswz<D>(row)) * 16);
+  }
+  auto issue = [&](u32x4* dst, const uint16_t* src, int kv0) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(N - kv0) * RB), kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) lds_load16(r, dst + (wave * NLD + i) * 64, koff[i]);
+  };
+
+  f32x16 dqa[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqa[db][i] = 0.0f;
+
+  auto compute = [&](const u32x4* Kt, const u32x4* Vt, int j) __attribute__((always_inline)) {
+    f32x16 s[NKB], dp[NKB];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const f32x16 z = {};
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, bwd::row_frag<D>(Kt, kb, kk, c32, h)), qf[kk], kk == 0 ? z : s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, bwd::row_frag<D>(Vt, kb, kk, c32, h)), dof[kk], kk == 0 ? z : dp[kb], 0, 0, 0);
+      }
+    // element (kb, i) holds key j*BN + 32kb + 8h + kofs(i) of query qrow
+    const int kv0 = j * BN;
+    if (kv0 + BN > N || (CAUSAL && kv0 + BN - 1 > wave_q0)) {
+      const int lim = (CAUSAL ? min(N - 1, qrow) : N - 1) - kv0 - 8 * h;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kofs = 32 * kb + 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
+          if (kofs > lim) s[kb][i] = neg_inf();
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], a.c, -lse2));
+        s[kb][i] = p * (dp[kb][i] - delta);  // dS^T
+      }
+    bf16x8 dsf[NCC];
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) dsf[cc] = bwd::pack8(s[cc >> 1], (cc & 1) * 8);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc)
+        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bwd::tr_frag<D>(Kt, db, cc, lane)),
+                                                          dsf[cc], dqa[db], 0, 0, 0);
+  };
+
+  __syncthreads();  // zeroed tiles visible before any load lands
+  if (n_tiles > 0) {
+    issue(kA, Kg, 0);
+    issue(vA, Vg, 0);
+  }
+  auto step = [&](int j, const u32x4* Kt, const u32x4* Vt, u32x4* Kn, u32x4* Vn) __attribute__((always_inline)) {
+    // the explicit wait: this compiler can drop the wait for tile loads at a
+    // barrier heading a loop
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 < n_tiles) {
+      issue(Kn, Kg, (j + 1) * BN);
+      issue(Vn, Vg, (j + 1) * BN);
+    }
+    if (j < n_vis) compute(Kt, Vt, j);
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, kA, vA, kB, vB);
+    if (j + 1 < n_tiles) step(j + 1, kB, vB, kA, vA);
+  }
+
+  if (qrow < N) bwd::store_rows((uint16_t*)a.dq + head + (size_t)qrow * D, dqa, h, a.scale);
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV: 4 waves x 32 keys; 64-query Q and dO tiles streamed through
+// double-buffered LDS, with the queries' log-sum-exps (in log2 units) and
+// Delta.  Per tile and wave: 16 MFMAs S = Q K^T (queries on the MFMA rows,
+// permuted by swap23 so each lane's values of one key come in runs of 8
+// consecutive queries; this lane's key on the columns), 16 MFMAs dP = dO V^T,
+// the elementwise P = exp2(c s - LSE log2 e) and dS = P (dP - Delta), then 16
+// MFMAs dV^T += dO^T P and 16 MFMAs dK^T += Q^T dS with dO^T and Q^T read
+// transposed.  Queries past N are masked like keys after the query under the
+// causal mask, so their weights and dS are 0 whatever their tile rows hold.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int BQ = 64, RB = D * 2, CPR = D / 8, RPB = 64 / CPR, TILE16 = BQ * CPR;
+  constexpr int NLD = TILE16 / 64 / 4, NKB = BQ / 32, NDB = D / 32, NKK = D / 16, NCC = BQ / 16;
+  __shared__ u32x4 qA[TILE16], qB[TILE16], gA[TILE16], gB[TILE16];
+  __shared__ f32x4 lA[BQ / 4], lB[BQ / 4], dA[BQ / 4], dB[BQ / 4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, c32 = lane & 31;
+  const int N = a.n;
+  const int t = xcd_remap(blockIdx.x, a.n_blocks);
+  const int bh = t / a.n_blk;
+  const int kblk = t - bh * a.n_blk;  // causal: the first key blocks see the most queries
+  const int k0 = kblk * kBwdRows;
+  const size_t head = (size_t)bh * N * D;
+  const uint16_t* Qg = (const uint16_t*)a.q + head;
+  const uint16_t* Kg = (const uint16_t*)a.k + head;
+  const uint16_t* Vg = (const uint16_t*)a.v + head;
+  const uint16_t* dOg = (const uint16_t*)a.dout + head;
+  const float* Lg = a.lse + (size_t)bh * N;
+  const float* Dg = a.delta + (size_t)bh * N;
+
+  const int key = k0 + wave * 32 + c32;  // this lane's key
+  const int wave_k0 = k0 + wave * 32;
+  const int n_qt = (N + BQ - 1) / BQ;
+  const int t_first = CAUSAL ? k0 / BQ : 0;           // first query tile with a query >= k0
+  const int t_wave = CAUSAL ? wave_k0 / BQ : 0;       // first one with a query >= this wave's keys
+  const bool active = wave_k0 < N;
+
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < TILE16; i += kBwdThreads) qA[i] = qB[i] = gA[i] = gB[i] = z;
+  }
+
+  // this lane's key: K (signs flipped for a negative scale) and V as MFMA B fragments
+  bf16x8 kreg[NKK], vreg[NKK];
+  bwd::load_row(kreg, Kg, key, N, D, h, a.flip);
+  bwd::load_row(vreg, Vg, key, N, D, h, 0u);
+
+  uint32_t toff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int row = (wave * NLD + i) * RPB + lane / CPR;
+    toff[i] = row * RB + (((lane % CPR) ^ kswz<D>(row)) * 16);
+  }
+  // query tile t: Q and dO rows, and the rows' LSE and Delta (the first wave,
+  // 4 bytes a lane), all by buffer-to-LDS loads
+  auto issue = [&](u32x4* qd, u32x4* gd, f32x4* ld, f32x4* dd, int tq) __attribute__((always_inline)) {
+    const int r0 = tq * BQ;
+    const uint32_t bytes = (uint32_t)(N - r0) * RB;
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Qg + (size_t)r0 * D), (short)0, (int)bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rg =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(dOg + (size_t)r0 * D), (short)0, (int)bytes, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      lds_load16(rq, qd + (wave * NLD + i) * 64, toff[i]);
+      lds_load16(rg, gd + (wave * NLD + i) * 64, toff[i]);
+    }
+    if (wave == 0) {
+      const uint32_t fbytes = (uint32_t)(N - r0) * 4;
+      const __amdgpu_buffer_rsrc_t rl =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Lg + r0), (short)0, (int)fbytes, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rd =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Dg + r0), (short)0, (int)fbytes, kRsrcWord3);
+      lds_load4(rl, (float*)ld, (uint32_t)lane * 4);
+      lds_load4(rd, (float*)dd, (uint32_t)lane * 4);
+    }
+  };
+
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dka[db][i] = dva[db][i] = 0.0f;
+
+  auto compute = [&](const u32x4* Qt, const u32x4* Gt, const f32x4* Lt, const f32x4* Dt, int tq)
+      __attribute__((always_inline)) {
+    f32x16 s[NKB], dp[NKB];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const f32x16 z = {};
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, bwd::row_frag<D>(Qt, kb, kk, c32, h)), kreg[kk], kk == 0 ? z : s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, bwd::row_frag<D>(Gt, kb, kk, c32, h)), vreg[kk], kk == 0 ? z : dp[kb], 0, 0, 0);
+      }
+    // element (kb, i) holds query tq*BQ + qofs(kb, i) of this lane's key, with
+    // qofs = 32kb + 8h + 16(i>>3) + 4((i>>2)&1) + (i&3): runs of 4 consecutive rows
+    const bool masked = (CAUSAL && tq * BQ < wave_k0 + 31) || tq * BQ + BQ > N;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int q4 = (32 * kb + 8 * h + 16 * (g >> 1) + 4 * (g & 1)) / 4;
+        const f32x4 ln = Lt[q4], dl = Dt[q4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g + e;
+          const int qg = tq * BQ + 4 * q4 + e;
+          float sv = s[kb][i];
+          if (masked && (qg >= N || (CAUSAL && qg < key))) sv = neg_inf();
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, a.c, -ln[e] * kLog2e));
+          s[kb][i] = p;
+          dp[kb][i] = p * (dp[kb][i] - dl[e]);
+        }
+      }
+    bf16x8 pf[NCC], dsf[NCC];
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+      pf[cc] = bwd::pack8(s[cc >> 1], (cc & 1) * 8);
+      dsf[cc] = bwd::pack8(dp[cc >> 1], (cc & 1) * 8);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) {
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bwd::tr_frag<D>(Gt, db, cc, lane)),
+                                                          pf[cc], dva[db], 0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bwd::tr_frag<D>(Qt, db, cc, lane)),
+                                                          dsf[cc], dka[db], 0, 0, 0);
+      }
+  };
+
+  __syncthreads();  // zeroed tiles visible before any load lands
+  if (t_first < n_qt) issue(qA, gA, lA, dA, t_first);
+  auto step = [&](int tq, const u32x4* Qt, const u32x4* Gt, const f32x4* Lt, const f32x4* Dt, u32x4* Qn,
+                  u32x4* Gn, f32x4* Ln, f32x4* Dn) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);  // see the dQ kernel
+    __syncthreads();
+    if (tq + 1 < n_qt) issue(Qn, Gn, Ln, Dn, tq + 1);
+    if (active && tq >= t_wave) compute(Qt, Gt, Lt, Dt, tq);
+  };
+  for (int tq = t_first; tq < n_qt; tq += 2) {
+    step(tq, qA, gA, lA, dA, qB, gB, lB, dB);
+    if (tq + 1 < n_qt) step(tq + 1, qB, gB, lB, dB, qA, gA, lA, dA);
+  }
+
+  if (key < N) {
+    bwd::store_rows((uint16_t*)a.dk + head + (size_t)key * D, dka, h, a.scale);
+    bwd::store_rows((uint16_t*)a.dv + head + (size_t)key * D, dva, h, 1.0f);
+  }
+}
+
+}  // namespace fa

@@ -158,9 +158,54 @@ fa_status check_split_call(const void* q, const void* k, const void* v, const vo
   return FA_OK;
 }
 
+fa_status check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, fa_sizes* sizes) {
+  fa_sizes sz;
+  fa_status st = check_shape(B, H, N, D, dtype, &sz);
+  if (st != FA_OK) return st;
+  sz.workspace_bytes = sz.lse_bytes;
+  if (sizes) *sizes = sz;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  return check_supported(B, H, N, D);
+}
+
+fa_status check_bwd_call(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const void* lse, const void* dq, const void* dk, const void* dv, const void* workspace,
+                         size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t D, float scale,
+                         int dtype) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL_POINTER;
+  fa_sizes sz;
+  fa_status st = check_bwd_shape(B, H, N, D, dtype, &sz);
+  if (st != FA_OK && st != FA_ERR_UNSUPPORTED) return st;
+  if (!std::isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (st == FA_ERR_UNSUPPORTED) return st;
+  const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if ((uintptr_t)p % 16 != 0) return FA_ERR_MISALIGNED;
+  if (workspace_bytes < sz.workspace_bytes) return FA_ERR_WORKSPACE;
+  // outputs and workspace may not overlap any buffer or each other; inputs may alias
+  struct Buf { const void* p; size_t n; };
+  const Buf outs[4] = {{dq, sz.q_bytes}, {dk, sz.q_bytes}, {dv, sz.q_bytes}, {workspace, sz.workspace_bytes}};
+  const Buf ins[6] = {{q, sz.q_bytes}, {k, sz.q_bytes}, {v, sz.q_bytes}, {o, sz.q_bytes}, {dout, sz.q_bytes},
+                      {lse, sz.lse_bytes}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return FA_ERR_ALIASING;
+    for (const Buf& b : ins)
+      if (overlaps(outs[i].p, outs[i].n, b.p, b.n)) return FA_ERR_ALIASING;
+  }
+  return FA_OK;
+}
+
 }  // namespace fa
 
 extern "C" {
+
+__attribute__((visibility("default"))) fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D,
+                                                               int causal, fa_dtype dtype, fa_sizes* out) {
+  (void)causal;
+  if (!out) return FA_ERR_NULL_POINTER;
+  return fa::check_bwd_shape(B, H, N, D, (int)dtype, out);
+}
 
 __attribute__((visibility("default"))) fa_status fa_fwd_split_query(int64_t B, int64_t H, int64_t Nq,
                                                                      int64_t Nk, int64_t D, int causal,
@@ -188,7 +233,7 @@ __attribute__((visibility("default"))) const char* fa_status_str(fa_status s) {
     case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE: scale must be finite";
     case FA_ERR_BAD_DTYPE: return "FA_ERR_BAD_DTYPE: dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16";
     case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: every pointer must be 16-byte aligned";
-    case FA_ERR_ALIASING: return "FA_ERR_ALIASING: o and lse must not overlap the inputs or each other";
+    case FA_ERR_ALIASING: return "FA_ERR_ALIASING: outputs and workspace must not overlap the inputs or each other";
     case FA_ERR_UNSUPPORTED:
       return "FA_ERR_UNSUPPORTED: needs D in {64,128}, N*D < 2^31, at most 2^31-1 workgroups, a gfx950 device";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call failed";

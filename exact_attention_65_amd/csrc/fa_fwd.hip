@@ -20,6 +20,7 @@
 
 #include "fa.h"
 #include "fa_check.h"
+#include "fa_device.h"
 #include "fa_fwd_kernel.hpp"
 
 namespace fa {
@@ -100,6 +101,8 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* o, float* l
   return a;
 }
 
+}  // namespace
+
 fa_status device_check() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
@@ -107,7 +110,6 @@ fa_status device_check() {
   return FA_OK;
 }
 
-}  // namespace
 }  // namespace fa
 
 extern "C" __attribute__((visibility("default"))) fa_status fa_fwd(

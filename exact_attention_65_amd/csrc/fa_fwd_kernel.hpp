@@ -194,6 +194,11 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, u32x4* lds,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// 4 bytes per lane likewise: the wave's 64 lanes fill 256 bytes at lds.
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, float* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+}
+
 // Work split: 4 waves x 32 query rows (128 rows per workgroup), two
 // workgroups per CU (one wave of each per SIMD).  Each wave runs its own
 // software pipeline over the key tiles so that its matrix-core work and its

@@ -26,8 +26,10 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-# tensor ids inside the seed key
-T_Q, T_K, T_V = 0, 1, 2
+# tensor ids inside the seed key; T_DO is the upstream gradient of the output
+# (the gradients' input: standard normal like the others, never scaled by the
+# peaked variant)
+T_Q, T_K, T_V, T_DO = 0, 1, 2, 3
 # variant ids
 PLAIN, PEAKED = 0, 1
 PEAK_FACTOR = 4.0  # exact in binary: multiplying before rounding loses nothing extra
@@ -74,8 +76,8 @@ class Workload:
         return 2.0 * self.B * self.H * self.N * self.D * (2 if self.dtype == "bf16" else 4)
 
     def rows(self, t: int) -> int:
-        """Rows of tensor t in one head: nq for Q, N for K and V."""
-        return self.nq if t == T_Q else self.N
+        """Rows of tensor t in one head: nq for Q and dO, N for K and V."""
+        return self.nq if t in (T_Q, T_DO) else self.N
 
     def with_variant(self, variant: int) -> "Workload":
         return Workload(self.name + ("_peaked" if variant == PEAKED else ""), self.seed_id,
@@ -143,8 +145,8 @@ def _stream(seed_id: int, variant: int, b: int, h: int, t: int) -> np.random.Gen
 
 
 def head_tensor(w: Workload, b: int, h: int, t: int) -> np.ndarray:
-    """One [rows, D] slice of tensor t (T_Q/T_K/T_V) as float32 values of w.dtype
-    (rows = nq for Q, N for K and V)."""
+    """One [rows, D] slice of tensor t (T_Q/T_K/T_V/T_DO) as float32 values of w.dtype
+    (rows = nq for Q and dO, N for K and V)."""
     x = _stream(w.seed_id, w.variant, b, h, t).standard_normal((w.rows(t), w.D), dtype=np.float32)
     if w.variant == PEAKED and t in (T_Q, T_K):
         x *= np.float32(PEAK_FACTOR)

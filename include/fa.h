@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 /* Identical to hipStream_t.  NULL means the device's null stream. */
 typedef struct ihipStream_t* fa_stream_t;
@@ -64,7 +64,7 @@ typedef enum fa_status {
   FA_ERR_UNSUPPORTED = 7,  /* valid but not built: D not 64/128, N*D >= 2^31, more   */
                            /* than 2^31-1 workgroups, or the device is not gfx950     */
   FA_ERR_HIP = 8,          /* a HIP runtime call failed (no device, launch failure)   */
-  FA_ERR_WORKSPACE = 9     /* fa_fwd_split: workspace_bytes below what the call needs */
+  FA_ERR_WORKSPACE = 9     /* workspace_bytes below what the call needs               */
 } fa_status;
 
 /* Byte sizes of every buffer of one call. */
@@ -177,6 +177,47 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
                        int64_t Nk, int64_t D, int causal, float scale, int n_splits, fa_dtype dtype,
                        fa_stream_t stream);
+
+/*
+ * fa_bwd_query - buffer sizes of an fa_bwd call.
+ *
+ * Pure host function.  q_bytes .. o_bytes are the sizes of q, k, v, o (and of
+ * dout, dq, dk, dv, which share them), lse_bytes that of lse, and
+ * workspace_bytes = B*H*N*4 (one float per query row: sum_d dO O).  Returns as
+ * fa_fwd_query; FA_ERR_UNSUPPORTED also for float32 (the backward is bfloat16
+ * only).
+ */
+fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, fa_dtype dtype,
+                       fa_sizes* out);
+
+/*
+ * fa_bwd - gradients of fa_fwd's O with respect to q, k and v, enqueued on `stream`.
+ *
+ * For the upstream gradient dout of O (LSE receives none), with the forward's
+ * o and lse: P = exp(scale q k^T - lse) over the visible keys,
+ * Delta = rowsum(dout * o), dS = P * (dout v^T - Delta), and
+ *     dq = scale dS k,   dk = scale dS^T q,   dv = P^T dout.
+ * The pages say the gradients are computed in a second pass over the same
+ * chunks without storing the score matrix (johe.ru, section "Стадии
+ * вычисления"); the formulas are the derivatives of the forward.  Two kernels
+ * on `stream`: one per 128 query rows (dq, and Delta into the workspace), then
+ * one per 128 keys (dk, dv).  No atomics: the result is deterministic.
+ *
+ * q, k, v, o, dout : [B, H, N, D] bfloat16 contiguous, read only (may alias).
+ * lse              : float32 [B, H, N] from fa_fwd with the same q, k, v,
+ *                    causal and scale.
+ * dq, dk, dv       : [B, H, N, D] bfloat16, written; not overlapping any other
+ *                    buffer.
+ * workspace        : >= fa_bwd_query's workspace_bytes, 16-byte aligned,
+ *                    caller-owned, clobbered.
+ *
+ * Validation and asynchrony as in fa_fwd; FA_ERR_WORKSPACE when
+ * workspace_bytes is too small.  bfloat16, D in {64, 128}.  Allocates nothing.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale, fa_dtype dtype,
+                 fa_stream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);

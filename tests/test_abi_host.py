@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert fa.fa_abi_version() == 2
+    assert fa.fa_abi_version() == 3
     for st in range(10):
         s = fa.fa_status_str(st)
         assert s.startswith("FA_")
@@ -144,8 +144,8 @@ def test_every_kernel_stub_is_defined():
     undefined = [l for l in out.splitlines() if " U " in l and "_ZN2fa" in l]
     assert undefined == []
     kernels = set(re.findall(r"(_ZN2fa\d+fa_\w+_kernelI\w+)", out))
-    # bf16: D x causal x split; fp32: D x causal; merge: D
-    assert len(kernels) == 8 + 4 + 2, kernels
+    # bf16: D x causal x split; fp32: D x causal; merge: D; backward: 2 kernels x D x causal
+    assert len(kernels) == 8 + 4 + 2 + 8, kernels
 
 
 # ---------------------------------------------------------------- fa_fwd_split
@@ -220,3 +220,54 @@ def test_split_validation_before_any_device_call(kw, expect):
     if expect == fa.FA_ERR_HIP and gpu_visible():
         pytest.skip("valid arguments would launch on fake addresses when a GPU is visible")
     assert split_call(**kw) == expect
+
+
+# ---------------------------------------------------------------- fa_bwd
+def test_bwd_query_sizes():
+    st, sz = fa.fa_bwd_query(2, 32, 4096, 128, 1, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK
+    assert sz.q_bytes == sz.k_bytes == sz.v_bytes == sz.o_bytes == 2 * 32 * 4096 * 128 * 2
+    assert sz.lse_bytes == sz.workspace_bytes == 2 * 32 * 4096 * 4
+    assert fa.fa_bwd_query(1, 1, 256, 64, 0, fa.FA_DTYPE_F32)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_query(1, 1, 0, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
+    assert fa.fa_bwd_query(1, 1, 256, 64, 0, 9)[0] == fa.FA_ERR_BAD_DTYPE
+    assert fa.lib().fa_bwd_query(1, 1, 256, 64, 0, 1, None) == fa.FA_ERR_NULL_POINTER
+
+
+BN_ = 100 * 64 * 2 * 2  # bytes of one [1, 2, 100, 64] bf16 tensor
+WSB = 2 * 100 * 4       # workspace of the default bwd_call
+
+
+def bwd_call(q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, do=A + 4 * SZ, lse=A + 5 * SZ, dq=A + 6 * SZ,
+             dk=A + 7 * SZ, dv=A + 8 * SZ, ws=A + 9 * SZ, ws_bytes=WSB, B=1, H=2, N=100, D=64, causal=1,
+             scale=0.125, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, N, D, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), fa.FA_ERR_HIP),                              # valid: fails only at the device query
+    (dict(k=A, v=A, o=A), fa.FA_ERR_HIP),                 # read-only inputs may alias
+    (dict(q=0), fa.FA_ERR_NULL_POINTER),
+    (dict(do=0), fa.FA_ERR_NULL_POINTER),
+    (dict(dv=0), fa.FA_ERR_NULL_POINTER),
+    (dict(ws=0), fa.FA_ERR_NULL_POINTER),
+    (dict(ws_bytes=WSB - 1), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 9 * SZ + 4), fa.FA_ERR_MISALIGNED),
+    (dict(dk=A + 7 * SZ + 8), fa.FA_ERR_MISALIGNED),
+    (dict(dq=A), fa.FA_ERR_ALIASING),                     # dq on top of q
+    (dict(dk=A + 6 * SZ + BN_ - 16), fa.FA_ERR_ALIASING),  # dk starts in dq's last 16 bytes
+    (dict(dk=A + 6 * SZ + BN_), fa.FA_ERR_HIP),           # dk right after dq: valid
+    (dict(dv=A + 4 * SZ), fa.FA_ERR_ALIASING),            # dv on top of dout
+    (dict(ws=A + 5 * SZ), fa.FA_ERR_ALIASING),            # workspace on top of lse
+    (dict(ws=A + 8 * SZ + 16), fa.FA_ERR_ALIASING),       # workspace inside dv
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE),
+    (dict(N=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=4), fa.FA_ERR_BAD_DTYPE),
+])
+def test_bwd_validation_before_any_device_call(kw, expect):
+    if expect == fa.FA_ERR_HIP and gpu_visible():
+        pytest.skip("valid arguments would launch on fake addresses when a GPU is visible")
+    assert bwd_call(**kw) == expect

@@ -1,0 +1,157 @@
+"""fa_bwd against the fp64 gradient oracle (oracle.attention_bwd_ref).
+
+The device path is the one a training step takes: fa_fwd produces O and LSE,
+fa_bwd the gradients; the oracle starts from the same bf16 inputs q, k, v, dO
+and computes everything in float64.
+
+Tolerance (per head and per gradient g in dq, dk, dv; g_ref the oracle's):
+  ||g - g_ref||_F <= 1e-2 ||g_ref||_F   and   max|g - g_ref| <= 2e-2 max|g_ref|.
+Every product in the kernels accumulates in fp32; the error comes from four
+bf16 roundings, each with unit roundoff u = 2^-9: P and dS as MFMA operands,
+the forward's bf16 O inside Delta = rowsum(dO O), and the stored gradient.
+Each contributes a relative error of at most u per term, with random signs
+over the contraction, so the norm-wise error stays at a few u (1e-2 ~ 5u) and
+the largest entry within 2e-2 ~ 10u of the largest reference entry.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_65_amd as fa
+import fa_inputs as fi
+from oracle import attention_bwd_ref, attention_ref
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+REL_FRO = 1e-2
+REL_MAX = 2e-2
+
+
+def _dout(w):
+    return gu.to_device_bits(fi.full_tensor(w, fi.T_DO), w.dtype)
+
+
+def _backward(w, q, k, v, do, scale, o=None, lse=None):
+    if o is None:
+        o, lse = fa.attention_forward(q, k, v, causal=w.causal, scale=scale)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, causal=w.causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _grad_errors(gpu, ref):
+    g = np.asarray(gpu, dtype=np.float64)
+    diff = np.abs(g - ref)
+    nref, mref = float(np.linalg.norm(ref)), float(np.abs(ref).max())
+    return dict(fro=float(np.linalg.norm(diff)) / nref if nref > 0 else float(np.abs(g).max()),
+                max=float(diff.max()) / mref if mref > 0 else float(np.abs(g).max()),
+                finite=bool(np.all(np.isfinite(g))))
+
+
+def _compare(w, grads, heads, scale, what):
+    worst = {n: dict(fro=0.0, max=0.0) for n in ("dq", "dk", "dv")}
+    for b, h in heads:
+        q, k, v = fi.head_qkv(w, b, h)
+        do = fi.head_tensor(w, b, h, fi.T_DO)
+        refs = attention_bwd_ref(q, k, v, do, w.causal, scale)
+        for name, g, ref in zip(("dq", "dk", "dv"), grads, refs):
+            e = _grad_errors(g[b, h].float().cpu().numpy(), ref)
+            assert e["finite"], f"{what} {name} (b={b}, h={h}): non-finite gradient"
+            worst[name]["fro"] = max(worst[name]["fro"], e["fro"])
+            worst[name]["max"] = max(worst[name]["max"], e["max"])
+    gu.log(f"  {what}: " + " ".join(f"{n} fro={e['fro']:.2e} max={e['max']:.2e}" for n, e in worst.items()))
+    gu.record(dict(case=what, kind="backward", **{f"{n}_{k}": v for n, e in worst.items() for k, v in e.items()}))
+    for n, e in worst.items():
+        assert e["fro"] <= REL_FRO, f"{what} {n}: relative Frobenius error {e['fro']} > {REL_FRO}"
+        assert e["max"] <= REL_MAX, f"{what} {n}: relative max error {e['max']} > {REL_MAX}"
+    return worst
+
+
+SMALL_N = [1, 17, 64, 65, 128, 129, 200, 333, 1000]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", SMALL_N)
+def test_backward_small_shapes(N, causal, D):
+    w = fi.Workload(f"bwd_n{N}_d{D}", 700 + SMALL_N.index(N) * 4 + D // 64, 1, 2, N, D, "bf16", causal)
+    gu.log(f"[gpu] backward N={N} D={D} causal={causal}")
+    q, k, v = gu.workload_tensors(w)
+    grads = _backward(w, q, k, v, _dout(w), w.scale)
+    _compare(w, grads, [(0, 0), (0, 1)], w.scale, f"{w.name} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.3, 1e-3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_other_scales(scale, causal):
+    """A negative scale (signs carried by Q in one kernel, by K in the other), a
+    large one and a nearly uniform one."""
+    w = fi.Workload("bwd_scale_n300_d128", 760, 1, 2, 300, 128, "bf16", causal)
+    gu.log(f"[gpu] backward scale={scale} causal={causal}")
+    q, k, v = gu.workload_tensors(w)
+    grads = _backward(w, q, k, v, _dout(w), scale)
+    _compare(w, grads, [(0, 0), (0, 1)], scale, f"{w.name} scale={scale} causal={causal}")
+
+
+def test_backward_zero_scale():
+    """scale 0: uniform weights, so dq = dk = 0 exactly and dv = P^T dO."""
+    w = fi.Workload("bwd_scale0_n257_d64", 761, 1, 2, 257, 64, "bf16", True)
+    q, k, v = gu.workload_tensors(w)
+    dq, dk, dv = _backward(w, q, k, v, _dout(w), 0.0)
+    assert torch.count_nonzero(dq).item() == 0 and torch.count_nonzero(dk).item() == 0
+    for h in range(2):
+        _, _, dv_ref = attention_bwd_ref(*fi.head_qkv(w, 0, h), fi.head_tensor(w, 0, h, fi.T_DO), True, 0.0)
+        e = _grad_errors(dv[0, h].float().cpu().numpy(), dv_ref)
+        assert e["fro"] <= REL_FRO and e["max"] <= REL_MAX, e
+
+
+def test_backward_peaked_scores():
+    """Scores 16x larger (Q and K scaled by 4): nearly one-hot weights."""
+    w = fi.CAUSAL_SWEEP[0].with_variant(fi.PEAKED)
+    w = fi.Workload(w.name + "_h4", w.seed_id, 1, 4, w.N, w.D, w.dtype, True, fi.PEAKED)
+    gu.log(f"[gpu] backward workload {w.name}")
+    q, k, v = gu.workload_tensors(w)
+    grads = _backward(w, q, k, v, _dout(w), w.scale)
+    _compare(w, grads, [(0, h) for h in range(w.H)], w.scale, w.name)
+
+
+def test_backward_with_oracle_forward():
+    """O and LSE from the oracle (O rounded to bf16) instead of fa_fwd: the
+    backward kernels alone against the oracle."""
+    w = fi.Workload("bwd_oraclefwd_n777_d128", 762, 1, 2, 777, 128, "bf16", True)
+    q, k, v = gu.workload_tensors(w)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, w.N), dtype=torch.float32, device=q.device)
+    for h in range(2):
+        o_ref, lse_ref = attention_ref(*fi.head_qkv(w, 0, h), True, w.scale)
+        o[0, h] = gu.to_device_values(fi.bf16_round(o_ref.astype(np.float32)), "bf16")
+        lse[0, h] = torch.from_numpy(lse_ref.astype(np.float32)).cuda()
+    grads = _backward(w, q, k, v, _dout(w), w.scale, o=o, lse=lse)
+    _compare(w, grads, [(0, 0), (0, 1)], w.scale, w.name)
+
+
+def test_backward_outputs_written_and_deterministic():
+    """Gradients pre-filled with NaN are fully overwritten; two runs agree bit for bit."""
+    w = fi.Workload("bwd_canary_n999_d128", 763, 2, 3, 999, 128, "bf16", True)
+    q, k, v = gu.workload_tensors(w)
+    do = _dout(w)
+    o, lse = fa.attention_forward(q, k, v, causal=True, scale=w.scale)
+    runs = []
+    for _ in range(2):
+        g = [torch.full_like(q, float("nan")) for _ in range(3)]
+        fa.attention_backward(q, k, v, o, lse, do, causal=True, scale=w.scale, dq=g[0], dk=g[1], dv=g[2])
+        torch.cuda.synchronize()
+        assert all(torch.isfinite(x.float()).all() for x in g)
+        runs.append([x.clone() for x in g])
+    assert all(torch.equal(a, b) for a, b in zip(*runs))
+
+
+@pytest.mark.parametrize("w", [fi.BF16_N4096, fi.CAUSAL_SWEEP[3]], ids=lambda w: w.name)
+def test_backward_full_size(w):
+    """The full-size workloads, in the launch configuration the benchmark
+    times; every element of seeded heads."""
+    gu.log(f"[gpu] backward workload {w.name}")
+    q, k, v = gu.workload_tensors(w)
+    grads = _backward(w, q, k, v, _dout(w), w.scale)
+    _compare(w, grads, fi.sample_heads(w, 2), w.scale, w.name + " backward")

@@ -19,12 +19,17 @@ def asm() -> str:
     return fabuild.device_asm("fa_fwd.hip")
 
 
+@pytest.fixture(scope="module")
+def bwd_asm() -> str:
+    return fabuild.device_asm("fa_bwd.hip")
+
+
 def _kernels(text: str):
     """(name, body) of every kernel in the assembly."""
     out = []
     for m in re.finditer(r"^(_ZN2fa\w*kernel\w*):", text, re.M):
         start = m.end()
-        end = text.find("s_endpgm", start)
+        end = text.find(".Lfunc_end", start)  # blocks may follow an s_endpgm
         out.append((m.group(1), text[start:end]))
     return out
 
@@ -64,3 +69,22 @@ def test_every_tile_barrier_drains_vmcnt(asm):
         assert waits, f"{name}: no barrier after a tile load"
         bad = [i for i, ok in waits if not ok]
         assert not bad, f"{name}: barrier(s) at asm line(s) {bad} do not wait for the LDS tile loads"
+
+
+def test_backward_kernels_present(bwd_asm):
+    names = [n for n, _ in _kernels(bwd_asm)]
+    assert sum("bwd_dq" in n for n in names) == 4, names
+    assert sum("bwd_dkdv" in n for n in names) == 4, names
+
+
+def test_backward_tile_barriers_drain_vmcnt(bwd_asm):
+    for name, body in _kernels(bwd_asm):
+        waits = _barrier_waits(body)
+        assert waits, f"{name}: no barrier after a tile load"
+        bad = [i for i, ok in waits if not ok]
+        assert not bad, f"{name}: barrier(s) at asm line(s) {bad} do not wait for the LDS tile loads"
+
+
+def test_backward_kernels_do_not_spill(bwd_asm):
+    for m in re.finditer(r"\.name:\s+(_ZN2fa\w*bwd\w*)\s.*?\.vgpr_spill_count:\s+(\d+)", bwd_asm, re.S):
+        assert int(m.group(2)) == 0, m.group(1)
