@@ -1,8 +1,9 @@
 // Host launcher and C entry point of the attention backward (see include/fa.h).
 //
 // Two launches on the caller's stream: fa_bwd_dq_kernel (one workgroup per 128
-// query rows: dq, and Delta = rowsum(dO O) into the workspace), then
-// fa_bwd_dkdv_kernel (one workgroup per 128 keys: dk, dv), which reads Delta.
+// query rows: dq, and per row Delta = rowsum(dO O) and -LSE log2(e) into the
+// workspace), then fa_bwd_dkdv_kernel (one workgroup per 128 keys: dk, dv),
+// which reads both.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -56,6 +57,7 @@ extern "C" __attribute__((visibility("default"))) fa_status fa_bwd(
   a.dk = dk;
   a.dv = dv;
   a.delta = (float*)workspace;
+  a.nlse2 = a.delta + B * H * N;
   a.n = (int)N;
   a.n_blk = (int)((N + fa::kBwdRows - 1) / fa::kBwdRows);
   a.n_blocks = (int)(B * H * a.n_blk);

@@ -33,6 +33,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;      // [B*H*N] workspace: sum_d dO O per row
+  float* nlse2;      // [B*H*N] workspace: -LSE log2(e) per row
   int n;             // sequence length N
   int n_blk;         // 128-row blocks per (b, h)
   int n_blocks;      // workgroups in the grid: B * H * n_blk
@@ -47,11 +48,27 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 namespace bwd {
 
-// Byte offset of 16-byte chunk `chunk` of tile row `row` (rows of D bf16,
-// chunks XOR-swizzled by kswz as in the forward's K tiles).
+// XOR applied to the 16-byte chunk index of tile row `row`.  Every tile here
+// is read both ways: 16 bytes a lane from 32 rows x 1 chunk (row_frag), and
+// transposed, 8 bytes a lane from 4 rows x 4 chunks (tr_frag).  With 64 banks
+// of 4 bytes both are conflict-free when the XOR is a bijection on the rows
+// that share a bank line and sends each aligned group of 4 rows to 4
+// different groups of 4 chunks:
+//   D = 128 (one row per line):  row = 4a + b  ->  4b + a  (a, b < 4);
+//   D = 64  (two rows per line): the 3 bits of (row >> 1) & 7 reversed.
+template <int D>
+__device__ __forceinline__ int bswz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else {
+    const int u = (row >> 1) & 7;
+    return ((u & 1) << 2) | (u & 2) | (u >> 2);
+  }
+}
+
+// Byte offset of 16-byte chunk `chunk` of tile row `row` (rows of D bf16).
 template <int D>
 __device__ __forceinline__ uint32_t chunk_addr(int row, int chunk) {
-  return (uint32_t)(row * D * 2 + ((chunk ^ kswz<D>(row)) * 16));
+  return (uint32_t)(row * D * 2 + ((chunk ^ bswz<D>(row)) * 16));
 }
 
 // A-operand rows of a 32-row MFMA block from a tile: row 32kb + swap23(c32),
@@ -64,7 +81,7 @@ __device__ __forceinline__ u32x4 row_frag(const u32x4* t, int kb, int kk, int c3
 
 // A-operand of the transposed tile (columns of the tile as MFMA rows): 32
 // columns 32db .. 32db+31, 16 rows 16cc .. 16cc+15, by two transposing reads
-// per lane; the lane layout is the forward's V^T read, here through kswz.
+// per lane; the lane layout is the forward's V^T read.
 template <int D>
 __device__ __forceinline__ u32x4 tr_frag(const u32x4* t, int db, int cc, int lane) {
   const int g = lane >> 4, i16 = lane & 15;
@@ -181,14 +198,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
     }
   }
   const float delta = pair_sum(dsum);
-  if (qrow < N && h == 0) a.delta[(size_t)bh * N + qrow] = delta;
   const float lse2 = qrow < N ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.0f;
+  if (qrow < N && h == 0) {
+    a.delta[(size_t)bh * N + qrow] = delta;
+    a.nlse2[(size_t)bh * N + qrow] = -lse2;
+  }
 
   uint32_t koff[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int row = (wave * NLD + i) * RPB + lane / CPR;
-    koff[i] = row * RB + (((lane % CPR) ^ kswz<D>(row)) * 16);
+    koff[i] = row * RB + (((lane % CPR) ^ bwd::bswz<D>(row)) * 16);
   }
   auto issue = [&](u32x4* dst, const uint16_t* src, int kv0) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
@@ -271,18 +291,28 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dK and dV: 4 waves x 32 keys; 64-query Q and dO tiles streamed through
-// double-buffered LDS, with the queries' log-sum-exps (in log2 units) and
-// Delta.  Per tile and wave: 16 MFMAs S = Q K^T (queries on the MFMA rows,
-// permuted by swap23 so each lane's values of one key come in runs of 8
-// consecutive queries; this lane's key on the columns), 16 MFMAs dP = dO V^T,
-// the elementwise P = exp2(c s - LSE log2 e) and dS = P (dP - Delta), then 16
-// MFMAs dV^T += dO^T P and 16 MFMAs dK^T += Q^T dS with dO^T and Q^T read
-// transposed.  Queries past N are masked like keys after the query under the
-// causal mask, so their weights and dS are 0 whatever their tile rows hold.
+// double-buffered LDS, with the rows' -LSE log2(e) and Delta.  Per tile and
+// wave, two phases of MFMA slots (one MFMA each):
+//   score phase     S = Q K^T and dP = dO V^T, block kb = 0 then 1 (32 query
+//                   rows each, permuted by swap23 so that each lane's values
+//                   of one key come in runs of 8 consecutive queries; this
+//                   lane's key on the columns);
+//   gradient phase  dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
+//                   transposed, query steps cc = 0 .. 3.
+// The elementwise P = exp2(c s - LSE log2 e), dS = P (dP - Delta) and the bf16
+// packing of block 0 run beside block 1's score MFMAs, those of block 1 beside
+// the gradient MFMAs of block 0's steps; LDS operands are read PF slots ahead.
+// Queries past N (and, under the causal mask, before the key) get weight 0.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BQ = 64, RB = D * 2, CPR = D / 8, RPB = 64 / CPR, TILE16 = BQ * CPR;
   constexpr int NLD = TILE16 / 64 / 4, NKB = BQ / 32, NDB = D / 32, NKK = D / 16, NCC = BQ / 16;
+  constexpr int NSS = 2 * NKB * NKK;  // score-phase slots
+  constexpr int NSG = 2 * NDB * NCC;  // gradient-phase slots
+  constexpr int PF = 4;               // operand reads in flight
+  constexpr int EPS = 16 / (NSS / 2); // softmax elements per slot (block 0 beside block 1's MFMAs)
+  constexpr int EPG = 16 / (NSG / 2); // softmax elements per slot (block 1 beside the gradient MFMAs)
+  static_assert(EPS * (NSS / 2) == 16 && EPG * (NSG / 2) == 16 && NKB == 2, "slot layout");
   __shared__ u32x4 qA[TILE16], qB[TILE16], gA[TILE16], gB[TILE16];
   __shared__ f32x4 lA[BQ / 4], lB[BQ / 4], dA[BQ / 4], dB[BQ / 4];
 
@@ -299,7 +329,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
   const uint16_t* Kg = (const uint16_t*)a.k + head;
   const uint16_t* Vg = (const uint16_t*)a.v + head;
   const uint16_t* dOg = (const uint16_t*)a.dout + head;
-  const float* Lg = a.lse + (size_t)bh * N;
+  const float* Lg = a.nlse2 + (size_t)bh * N;
   const float* Dg = a.delta + (size_t)bh * N;
 
   const int key = k0 + wave * 32 + c32;  // this lane's key
@@ -323,10 +353,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int row = (wave * NLD + i) * RPB + lane / CPR;
-    toff[i] = row * RB + (((lane % CPR) ^ kswz<D>(row)) * 16);
+    toff[i] = row * RB + (((lane % CPR) ^ bwd::bswz<D>(row)) * 16);
   }
-  // query tile t: Q and dO rows, and the rows' LSE and Delta (the first wave,
-  // 4 bytes a lane), all by buffer-to-LDS loads
+  // query tile t: Q and dO rows, and the rows' -LSE log2(e) and Delta (the
+  // first wave, 4 bytes a lane), all by buffer-to-LDS loads
   auto issue = [&](u32x4* qd, u32x4* gd, f32x4* ld, f32x4* dd, int tq) __attribute__((always_inline)) {
     const int r0 = tq * BQ;
     const uint32_t bytes = (uint32_t)(N - r0) * RB;
@@ -356,54 +386,104 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
 #pragma unroll
     for (int i = 0; i < 16; ++i) dka[db][i] = dva[db][i] = 0.0f;
 
+  // operand of score slot f: rows of block f / (2 NKK), chunk (f / 2) % NKK of
+  // Q (even f: S) or dO (odd f: dP); of gradient slot f: step f / (2 NDB),
+  // d block (f / 2) % NDB of dO^T (even f: dV) or Q^T (odd f: dK)
+  auto sfrag = [&](const u32x4* Qt, const u32x4* Gt, int f) __attribute__((always_inline)) {
+    return bwd::row_frag<D>((f & 1) ? Gt : Qt, f / (2 * NKK), (f / 2) % NKK, c32, h);
+  };
+  auto gfrag = [&](const u32x4* Qt, const u32x4* Gt, int f) __attribute__((always_inline)) {
+    return bwd::tr_frag<D>((f & 1) ? Qt : Gt, (f / 2) % NDB, f / (2 * NDB), lane);
+  };
+
   auto compute = [&](const u32x4* Qt, const u32x4* Gt, const f32x4* Lt, const f32x4* Dt, int tq)
       __attribute__((always_inline)) {
-    f32x16 s[NKB], dp[NKB];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const f32x16 z = {};
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, bwd::row_frag<D>(Qt, kb, kk, c32, h)), kreg[kk], kk == 0 ? z : s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, bwd::row_frag<D>(Gt, kb, kk, c32, h)), vreg[kk], kk == 0 ? z : dp[kb], 0, 0, 0);
-      }
-    // element (kb, i) holds query tq*BQ + qofs(kb, i) of this lane's key, with
-    // qofs = 32kb + 8h + 16(i>>3) + 4((i>>2)&1) + (i&3): runs of 4 consecutive rows
+    // tiles with a query past N or (causal) before one of the wave's keys
     const bool masked = (CAUSAL && tq * BQ < wave_k0 + 31) || tq * BQ + BQ > N;
+    const float c = a.c;
+    f32x16 s[NKB], dp[NKB];
+    bf16x8 pf[NCC], dsf[NCC];
+    // element (kb, i) holds query tq*BQ + 4 q4 + (i & 3) of this lane's key,
+    // q4 = 8kb + 2h + 4(i >> 3) + ((i >> 2) & 1)
+    auto q4_of = [&](int kb, int i) __attribute__((always_inline)) {
+      return 8 * kb + 2 * h + 4 * (i >> 3) + ((i >> 2) & 1);
+    };
+    // the rows' -LSE log2(e) and Delta, read before the tile's first MFMA so
+    // that no wait for them drains the operand reads in flight
+    f32x4 nl[NKB][4], dl[NKB][4];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int q4 = (32 * kb + 8 * h + 16 * (g >> 1) + 4 * (g & 1)) / 4;
-        const f32x4 ln = Lt[q4], dl = Dt[q4];
+        nl[kb][g] = Lt[q4_of(kb, 4 * g)];
+        dl[kb][g] = Dt[q4_of(kb, 4 * g)];
+      }
+    // a masked block's scores, once, before its first softmax element
+    auto mask_block = [&](int kb) __attribute__((always_inline)) {
+      if (masked) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          const int qg = tq * BQ + 4 * q4 + e;
-          float sv = s[kb][i];
-          if (masked && (qg >= N || (CAUSAL && qg < key))) sv = neg_inf();
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, a.c, -ln[e] * kLog2e));
-          s[kb][i] = p;
-          dp[kb][i] = p * (dp[kb][i] - dl[e]);
+        for (int i = 0; i < 16; ++i) {
+          const int qg = tq * BQ + 4 * q4_of(kb, i) + (i & 3);
+          if (qg >= N || (CAUSAL && qg < key)) s[kb][i] = neg_inf();
         }
       }
-    bf16x8 pf[NCC], dsf[NCC];
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) {
-      pf[cc] = bwd::pack8(s[cc >> 1], (cc & 1) * 8);
-      dsf[cc] = bwd::pack8(dp[cc >> 1], (cc & 1) * 8);
-    }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int cc = 0; cc < NCC; ++cc) {
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bwd::tr_frag<D>(Gt, db, cc, lane)),
-                                                          pf[cc], dva[db], 0, 0, 0);
-        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bwd::tr_frag<D>(Qt, db, cc, lane)),
-                                                          dsf[cc], dka[db], 0, 0, 0);
+    };
+    auto softmax_elem = [&](int kb, int i) __attribute__((always_inline)) {
+      const int g = i >> 2, e = i & 3;
+      const float sv = s[kb][i];
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, nl[kb][g][e]));
+      float ds = p * (dp[kb][i] - dl[kb][g][e]);
+      float pp = p;
+      pin(pp);
+      pin(ds);
+      s[kb][i] = pp;
+      dp[kb][i] = ds;
+      if ((i & 7) == 7) {
+        const int cc = 2 * kb + (i >> 3);
+        pf[cc] = bwd::pack8(s[kb], i & 8);
+        dsf[cc] = bwd::pack8(dp[kb], i & 8);
       }
+    };
+
+    u32x4 sf[NSS], gf[NSG];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) sf[k] = sfrag(Qt, Gt, k);
+    // score phase
+#pragma unroll
+    for (int k = 0; k < NSS; ++k) {
+      if (k + PF < NSS) sf[k + PF] = sfrag(Qt, Gt, k + PF);
+      else gf[k + PF - NSS] = gfrag(Qt, Gt, k + PF - NSS);
+      const int kb = k / (2 * NKK), kk = (k / 2) % NKK;
+      const f32x16 z = {};
+      if (k & 1)
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sf[k]), vreg[kk],
+                                                         kk == 0 ? z : dp[kb], 0, 0, 0);
+      else
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sf[k]), kreg[kk],
+                                                        kk == 0 ? z : s[kb], 0, 0, 0);
+      if (k == NSS / 2) mask_block(0);
+      if (k >= NSS / 2)
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) softmax_elem(0, (k - NSS / 2) * EPS + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // gradient phase
+#pragma unroll
+    for (int k = 0; k < NSG; ++k) {
+      if (k + PF < NSG) gf[k + PF] = gfrag(Qt, Gt, k + PF);
+      const int cc = k / (2 * NDB), db = (k / 2) % NDB;
+      if (k & 1)
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, gf[k]), dsf[cc], dka[db], 0,
+                                                          0, 0);
+      else
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, gf[k]), pf[cc], dva[db], 0,
+                                                          0, 0);
+      if (k == 0) mask_block(1);
+      if (k < NSG / 2)
+#pragma unroll
+        for (int e = 0; e < EPG; ++e) softmax_elem(1, k * EPG + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   __syncthreads();  // zeroed tiles visible before any load lands

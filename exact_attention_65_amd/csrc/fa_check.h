@@ -37,7 +37,7 @@ fa_status check_split_call(const void* q, const void* k, const void* v, const vo
                            int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int n_splits,
                            int dtype, int* splits);
 
-// fa_bwd_query: sizes (workspace: one float per query row).
+// fa_bwd_query: sizes (workspace: two floats per query row).
 fa_status check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, fa_sizes* sizes);
 
 // Full validation of an fa_bwd call, without touching the device.

@@ -183,9 +183,9 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
  *
  * Pure host function.  q_bytes .. o_bytes are the sizes of q, k, v, o (and of
  * dout, dq, dk, dv, which share them), lse_bytes that of lse, and
- * workspace_bytes = B*H*N*4 (one float per query row: sum_d dO O).  Returns as
- * fa_fwd_query; FA_ERR_UNSUPPORTED also for float32 (the backward is bfloat16
- * only).
+ * workspace_bytes = B*H*N*8 (two floats per query row: sum_d dO O and
+ * -LSE log2(e)).  Returns as fa_fwd_query; FA_ERR_UNSUPPORTED also for float32
+ * (the backward is bfloat16 only).
  */
 fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, fa_dtype dtype,
                        fa_sizes* out);
@@ -198,10 +198,12 @@ fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, f
  * Delta = rowsum(dout * o), dS = P * (dout v^T - Delta), and
  *     dq = scale dS k,   dk = scale dS^T q,   dv = P^T dout.
  * The pages say the gradients are computed in a second pass over the same
- * chunks without storing the score matrix (johe.ru, section "Стадии
- * вычисления"); the formulas are the derivatives of the forward.  Two kernels
- * on `stream`: one per 128 query rows (dq, and Delta into the workspace), then
- * one per 128 keys (dk, dv).  No atomics: the result is deterministic.
+ * chunks without storing the score matrix ("Flash Attention: ускорить
+ * attention в 6 раз без потери точности", section "Стадии вычисления"); the
+ * formulas are the derivatives of the forward.  Two kernels on `stream`: one
+ * per 128 query rows (dq, and per row Delta and the LSE in base 2 into the
+ * workspace), then one per 128 keys (dk, dv).  No atomics: the result is
+ * deterministic.
  *
  * q, k, v, o, dout : [B, H, N, D] bfloat16 contiguous, read only (may alias).
  * lse              : float32 [B, H, N] from fa_fwd with the same q, k, v,

@@ -227,7 +227,7 @@ def test_bwd_query_sizes():
     st, sz = fa.fa_bwd_query(2, 32, 4096, 128, 1, fa.FA_DTYPE_BF16)
     assert st == fa.FA_OK
     assert sz.q_bytes == sz.k_bytes == sz.v_bytes == sz.o_bytes == 2 * 32 * 4096 * 128 * 2
-    assert sz.lse_bytes == sz.workspace_bytes == 2 * 32 * 4096 * 4
+    assert sz.lse_bytes == 2 * 32 * 4096 * 4 and sz.workspace_bytes == 2 * sz.lse_bytes
     assert fa.fa_bwd_query(1, 1, 256, 64, 0, fa.FA_DTYPE_F32)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_bwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_bwd_query(1, 1, 0, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
@@ -236,7 +236,7 @@ def test_bwd_query_sizes():
 
 
 BN_ = 100 * 64 * 2 * 2  # bytes of one [1, 2, 100, 64] bf16 tensor
-WSB = 2 * 100 * 4       # workspace of the default bwd_call
+WSB = 2 * 2 * 100 * 4   # workspace of the default bwd_call
 
 
 def bwd_call(q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, do=A + 4 * SZ, lse=A + 5 * SZ, dq=A + 6 * SZ,
