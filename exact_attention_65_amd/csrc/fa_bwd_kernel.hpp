@@ -71,28 +71,38 @@ __device__ __forceinline__ uint32_t chunk_addr(int row, int chunk) {
   return (uint32_t)(row * D * 2 + ((chunk ^ bswz<D>(row)) * 16));
 }
 
-// A-operand rows of a 32-row MFMA block from a tile: row 32kb + swap23(c32),
-// columns 16kk + 8h .. +7 (one 16-byte chunk).
+// Per-lane LDS addresses of the two operand reads.  bswz depends on the row
+// only through bits 0..3, and a chunk index enters the byte address as
+// 16 * (chunk ^ bswz(row)), so the row block (kb, cc) adds a constant and the
+// column block (kk, db) XORs a constant into one per-lane base:
+//   row read (A rows 32kb + swap23(c32), columns 16kk + 8h .. +7):
+//       (rbase ^ (kk << 5)) + 32 kb RB
+//   transposed read (A rows = tile columns 32db .. +31, A columns = tile rows
+//   16cc + 8hh + r and +4; the lane layout of the forward's V^T read):
+//       (tbase[x] ^ (db << 6)) + 16 cc RB,  x = 0, 1 for the rows r and r + 4
 template <int D>
-__device__ __forceinline__ u32x4 row_frag(const u32x4* t, int kb, int kk, int c32, int h) {
-  const int row = 32 * kb + swap23(c32);
-  return *(const u32x4*)((const char*)t + chunk_addr<D>(row, 2 * kk + h));
+__device__ __forceinline__ uint32_t row_base(int c32, int h) {
+  return chunk_addr<D>(swap23(c32), h);
 }
-
-// A-operand of the transposed tile (columns of the tile as MFMA rows): 32
-// columns 32db .. 32db+31, 16 rows 16cc .. 16cc+15, by two transposing reads
-// per lane; the lane layout is the forward's V^T read.
 template <int D>
-__device__ __forceinline__ u32x4 tr_frag(const u32x4* t, int db, int cc, int lane) {
+__device__ __forceinline__ uint32_t tr_base(int lane, int x) {
   const int g = lane >> 4, i16 = lane & 15;
   const int hh = g >> 1, gg = g & 1, r = i16 >> 2, q = i16 & 3;
-  const int chunk = 4 * db + 2 * gg + (q >> 1);
-  const int row = 16 * cc + 8 * hh + r;
-  const char* base = (const char*)t + (q & 1) * 8;
+  return chunk_addr<D>(8 * hh + r + 4 * x, 2 * gg + (q >> 1)) + (q & 1) * 8;
+}
+
+template <int D>
+__device__ __forceinline__ u32x4 row_frag(const u32x4* t, uint32_t rbase, int kb, int kk) {
+  return *(const u32x4*)((const char*)t + ((rbase ^ (uint32_t)(kk << 5)) + kb * 32 * D * 2));
+}
+
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag(const u32x4* t, uint32_t tb0, uint32_t tb1, int db, int cc) {
+  const char* base = (const char*)t + cc * 16 * D * 2;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(base + chunk_addr<D>(row, chunk)));
+      (__attribute__((address_space(3))) i16x4*)(base + (tb0 ^ (uint32_t)(db << 6))));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(base + chunk_addr<D>(row + 4, chunk)));
+      (__attribute__((address_space(3))) i16x4*)(base + (tb1 ^ (uint32_t)(db << 6))));
   return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -143,7 +153,7 @@ __device__ __forceinline__ void store_rows(uint16_t* out_row, const f32x16 (&acc
 // Per tile and wave: 16 MFMAs S^T = K Q^T (keys on rows, this lane's query on
 // the columns: the forward's orientation), 16 MFMAs dP^T = V dO^T, the
 // elementwise dS^T = P^T (dP^T - Delta), and 16 MFMAs dQ^T += K^T dS^T with
-// K^T read transposed from the same tile.
+// K^T read transposed from the same tile (for D = 128; half as many for 64).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = 64, RB = D * 2, CPR = D / 8, RPB = 64 / CPR, TILE16 = BN * CPR;
@@ -223,46 +233,78 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqa[db][i] = 0.0f;
 
+  // operand of score slot f: rows of block f / (2 NKK), chunk (f / 2) % NKK of
+  // K (even f: S^T) or V (odd f: dP^T); of dQ slot f: key step f / NDB, d
+  // block f % NDB of K^T
+  const uint32_t rbase = bwd::row_base<D>(c32, h), tb0 = bwd::tr_base<D>(lane, 0), tb1 = bwd::tr_base<D>(lane, 1);
+  auto sfrag = [&](const u32x4* Kt, const u32x4* Vt, int f) __attribute__((always_inline)) {
+    return bwd::row_frag<D>((f & 1) ? Vt : Kt, rbase, f / (2 * NKK), (f / 2) % NKK);
+  };
+  auto gfrag = [&](const u32x4* Kt, int f) __attribute__((always_inline)) {
+    return bwd::tr_frag<D>(Kt, tb0, tb1, f % NDB, f / NDB);
+  };
+  // per tile and wave, two phases of MFMA slots: the score phase (S^T and
+  // dP^T, block kb = 0 then 1), then the dQ phase (key steps cc = 0 .. 3);
+  // block 0's elementwise dS^T runs beside block 1's score MFMAs, block 1's
+  // beside the dQ MFMAs of block 0's steps; LDS operands are read PF slots ahead
   auto compute = [&](const u32x4* Kt, const u32x4* Vt, int j) __attribute__((always_inline)) {
-    f32x16 s[NKB], dp[NKB];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const f32x16 z = {};
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, bwd::row_frag<D>(Kt, kb, kk, c32, h)), qf[kk], kk == 0 ? z : s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, bwd::row_frag<D>(Vt, kb, kk, c32, h)), dof[kk], kk == 0 ? z : dp[kb], 0, 0, 0);
-      }
-    // element (kb, i) holds key j*BN + 32kb + 8h + kofs(i) of query qrow
+    constexpr int NSS = 2 * NKB * NKK, NSG = NDB * NCC, PF = 4;
+    constexpr int EPS = 16 / (NSS / 2), EPG = 16 / (NSG / 2);
+    static_assert(EPS * (NSS / 2) == 16 && EPG * (NSG / 2) == 16 && NKB == 2, "slot layout");
     const int kv0 = j * BN;
-    if (kv0 + BN > N || (CAUSAL && kv0 + BN - 1 > wave_q0)) {
-      const int lim = (CAUSAL ? min(N - 1, qrow) : N - 1) - kv0 - 8 * h;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+    const bool masked = kv0 + BN > N || (CAUSAL && kv0 + BN - 1 > wave_q0);
+    f32x16 s[NKB], dp[NKB];
+    bf16x8 dsf[NCC];
+    // element (kb, i) holds key kv0 + 32kb + 8h + kofs(i) of query qrow
+    auto mask_block = [&](int kb) __attribute__((always_inline)) {
+      if (masked) {
+        const int lim = (CAUSAL ? min(N - 1, qrow) : N - 1) - kv0 - 8 * h;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kofs = 32 * kb + 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
           if (kofs > lim) s[kb][i] = neg_inf();
         }
+      }
+    };
+    auto ds_elem = [&](int kb, int i) __attribute__((always_inline)) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], a.c, -lse2));
+      float ds = p * (dp[kb][i] - delta);
+      pin(ds);
+      s[kb][i] = ds;
+      if ((i & 7) == 7) dsf[2 * kb + (i >> 3)] = bwd::pack8(s[kb], i & 8);
+    };
+    u32x4 sf[NSS], gf[NSG];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) sf[k] = sfrag(Kt, Vt, k);
+#pragma unroll
+    for (int k = 0; k < NSS; ++k) {
+      if (k + PF < NSS) sf[k + PF] = sfrag(Kt, Vt, k + PF);
+      else gf[k + PF - NSS] = gfrag(Kt, k + PF - NSS);
+      const int kb = k / (2 * NKK), kk = (k / 2) % NKK;
+      const f32x16 z = {};
+      if (k & 1)
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sf[k]), dof[kk],
+                                                         kk == 0 ? z : dp[kb], 0, 0, 0);
+      else
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sf[k]), qf[kk],
+                                                        kk == 0 ? z : s[kb], 0, 0, 0);
+      if (k == NSS / 2) mask_block(0);
+      if (k >= NSS / 2)
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) ds_elem(0, (k - NSS / 2) * EPS + e);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int k = 0; k < NSG; ++k) {
+      if (k + PF < NSG) gf[k + PF] = gfrag(Kt, k + PF);
+      const int cc = k / NDB, db = k % NDB;
+      dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, gf[k]), dsf[cc], dqa[db], 0, 0, 0);
+      if (k == 0) mask_block(1);
+      if (k < NSG / 2)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], a.c, -lse2));
-        s[kb][i] = p * (dp[kb][i] - delta);  // dS^T
-      }
-    bf16x8 dsf[NCC];
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) dsf[cc] = bwd::pack8(s[cc >> 1], (cc & 1) * 8);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int cc = 0; cc < NCC; ++cc)
-        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bwd::tr_frag<D>(Kt, db, cc, lane)),
-                                                          dsf[cc], dqa[db], 0, 0, 0);
+        for (int e = 0; e < EPG; ++e) ds_elem(1, k * EPG + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   __syncthreads();  // zeroed tiles visible before any load lands
@@ -389,11 +431,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
   // operand of score slot f: rows of block f / (2 NKK), chunk (f / 2) % NKK of
   // Q (even f: S) or dO (odd f: dP); of gradient slot f: step f / (2 NDB),
   // d block (f / 2) % NDB of dO^T (even f: dV) or Q^T (odd f: dK)
+  const uint32_t rbase = bwd::row_base<D>(c32, h), tb0 = bwd::tr_base<D>(lane, 0), tb1 = bwd::tr_base<D>(lane, 1);
   auto sfrag = [&](const u32x4* Qt, const u32x4* Gt, int f) __attribute__((always_inline)) {
-    return bwd::row_frag<D>((f & 1) ? Gt : Qt, f / (2 * NKK), (f / 2) % NKK, c32, h);
+    return bwd::row_frag<D>((f & 1) ? Gt : Qt, rbase, f / (2 * NKK), (f / 2) % NKK);
   };
   auto gfrag = [&](const u32x4* Qt, const u32x4* Gt, int f) __attribute__((always_inline)) {
-    return bwd::tr_frag<D>((f & 1) ? Qt : Gt, (f / 2) % NDB, f / (2 * NDB), lane);
+    return bwd::tr_frag<D>((f & 1) ? Qt : Gt, tb0, tb1, (f / 2) % NDB, f / (2 * NDB));
   };
 
   auto compute = [&](const u32x4* Qt, const u32x4* Gt, const f32x4* Lt, const f32x4* Dt, int tq)
