@@ -45,7 +45,7 @@ class Workload:
     H: int
     N: int
     D: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "fp8" (E4M3 codes with MX block scales: fa_inputs.fp8)
     causal: bool
     variant: int = PLAIN
     NQ: int = 0  # query rows per head; 0: as many as keys (N)
@@ -73,7 +73,7 @@ class Workload:
     @property
     def kv_bytes(self) -> float:
         """Bytes of K and V (the stream a decode step is bound by)."""
-        return 2.0 * self.B * self.H * self.N * self.D * (2 if self.dtype == "bf16" else 4)
+        return 2.0 * self.B * self.H * self.N * self.D * {"bf16": 2, "fp8": 1}.get(self.dtype, 4)
 
     def rows(self, t: int) -> int:
         """Rows of tensor t in one head: nq for Q and dO, N for K and V."""
@@ -105,8 +105,14 @@ SPLIT_CHUNK = Workload("bf16_chunk_b1_h32_nq512_nk8192_d128", 41, 1, 32, 8192, 1
 SPLIT_WORKLOADS = (SPLIT_DECODE, SPLIT_CHUNK)
 
 
+# FP8 inputs at the headline shape: Q, K, V drawn like the bf16 workload's and
+# quantised to E4M3 with MX block scales (fa_inputs.fp8).
+FP8_N4096 = Workload("fp8_b2_h32_n4096_d128", 6, 2, 32, 4096, 128, "fp8", False)
+FP8_WORKLOADS = (FP8_N4096,)
+
+
 def workload_by_name(name: str) -> Workload:
-    for w in ALL_WORKLOADS + SPLIT_WORKLOADS:
+    for w in ALL_WORKLOADS + SPLIT_WORKLOADS + FP8_WORKLOADS:
         if w.name == name:
             return w
     raise KeyError(name)

@@ -83,3 +83,16 @@ def test_workload_table():
     assert fi.CAUSAL_LONG.flops == 4 * 8 * 131072 ** 2 * 128 / 2
     assert len(fi.ALL_WORKLOADS) == 14
     assert fi.workload_by_name("bf16_causal_b1_h32_n512_d128_peaked").variant == fi.PEAKED
+
+
+def test_fp8_inputs_regenerate_per_head_and_fill_their_range():
+    import fa_inputs.fp8 as f8
+    w = fi.Workload("fp8_gen", 91, 2, 3, 77, 128, "fp8", False)
+    codes, scales = f8.full_mx(w, fi.T_K)
+    assert codes.shape == (2, 3, 77, 128) and scales.shape == (2, 3, 77, 4)
+    c, s = f8.head_mx(w, 1, 2, fi.T_K)
+    assert np.array_equal(codes[1, 2], c) and np.array_equal(scales[1, 2], s)
+    assert not np.any((codes & 0x7F) == 0x7F), "no NaN codes"
+    # every block's largest magnitude lands in the top binade of E4M3 ([256, 448])
+    mags = (codes & 0x7F).reshape(2, 3, 77, 4, 32).max(axis=-1)
+    assert np.all(mags >= 0x78)
