@@ -17,6 +17,10 @@ through fa_fwd_split: the range kernel and the merge kernel, both inside the
 timed events.  Their roofline is the HBM one (GB/s of Q, K, V, O and LSE) when
 the workload's arithmetic intensity is below the machine balance.
 
+The FP8 workload (fp8_b2_h32_n4096_d128: E4M3 inputs with MX block scales)
+steps through fa_fwd_fp8; its roofline peak is the combination of the fp8 and
+bf16 MFMA peaks (Q K^T runs on the first, P V on the second).
+
 With --backward a step is one fa_bwd call (its two kernels: dq with Delta, then
 dk and dv) for a seeded upstream gradient, O and LSE having been computed by
 fa_fwd before the timed region.  FLOPs are those of the five products of the
@@ -38,8 +42,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fwd attention TFLOP/s (4BHN²D, ÷2 causal) + % of bf16 MFMA peak, N=4096 D=128"
 HEADLINE = "bf16_b2_h32_n4096_d128"
-# MI355X published dense peaks (TFLOP/s): bf16 MFMA 2516.6 (= 2.5 PFLOP/s), fp32 MFMA 157.3
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+# MI355X published dense peaks (TFLOP/s): bf16 MFMA 2516.6 (= 2.5 PFLOP/s), fp8 5033.2, fp32 MFMA 157.3.
+# The FP8 path runs Q K^T on the fp8 matrix cores and P V on the bf16 ones, half of the FLOPs each:
+# its ceiling is the harmonic combination of the two peaks.
+PEAK_FP8_MIXED = 1.0 / (0.5 / 5033.2 + 0.5 / 2516.6)
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": PEAK_FP8_MIXED}
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 KERNEL_SOURCES = ["exact_attention_65_amd/csrc/fa_fwd_kernel.hpp", "exact_attention_65_amd/csrc/fa_fwd.hip"]
 BWD_FLOP_FACTOR = 2.5  # five N x N x D products against the forward's two
@@ -91,9 +98,15 @@ def cpu_baseline(w, budget_s: float = 12.0, backward: bool = False):
     for b, h in heads:
         q, k, v = fi.head_qkv(w, b, h)
         do = fi.head_tensor(w, b, h, fi.T_DO) if backward else None
+        if w.dtype == "fp8":
+            import fa_inputs.fp8 as f8
+            from oracle import attention_fp8_ref
+            mx = [f8.head_mx(w, b, h, t) for t in (fi.T_Q, fi.T_K, fi.T_V)]
         t0 = time.perf_counter()
         if backward:
             attention_bwd_ref(q, k, v, do, w.causal, w.scale)
+        elif w.dtype == "fp8":
+            attention_fp8_ref(*mx[0], *mx[1], *mx[2], w.causal, w.scale)
         else:
             attention_ref(q, k, v, w.causal, w.scale)
         t_total += time.perf_counter() - t0
@@ -144,7 +157,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    names = [w.name for w in fi.ALL_WORKLOADS + fi.SPLIT_WORKLOADS] if args.sweep else [args.workload]
+    names = [w.name for w in fi.ALL_WORKLOADS + fi.SPLIT_WORKLOADS + fi.FP8_WORKLOADS] if args.sweep \
+        else [args.workload]
     for name in names:
         w = fi.workload_by_name(name)
         split = args.split if args.split is not None else (fa.FA_SPLIT_AUTO if w.NQ > 0 else None)
@@ -152,18 +166,31 @@ def main():
             split = None
             if w.dtype != "bf16" or w.NQ > 0:
                 continue
+        if w.dtype == "fp8":
+            split = None
         if split is not None and w.dtype != "bf16":
             continue
         dt = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32
         tensors = []
-        for t in (fi.T_Q, fi.T_K, fi.T_V):
-            bits = fi.full_tensor(w, t)
-            x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" \
-                else torch.from_numpy(bits)
-            tensors.append(x.cuda())
-            del bits, x
-        q, k, v = tensors
-        o = torch.empty_like(q)
+        if w.dtype == "fp8":
+            import fa_inputs.fp8 as f8
+            scales = []
+            for t in (fi.T_Q, fi.T_K, fi.T_V):
+                codes, sc = f8.full_mx(w, t)
+                tensors.append(torch.from_numpy(codes).cuda())
+                scales.append(torch.from_numpy(sc).cuda())
+            q, k, v = tensors
+            qs, ks, vs = scales
+            o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        else:
+            for t in (fi.T_Q, fi.T_K, fi.T_V):
+                bits = fi.full_tensor(w, t)
+                x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" \
+                    else torch.from_numpy(bits)
+                tensors.append(x.cuda())
+                del bits, x
+            q, k, v = tensors
+            o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.nq), dtype=torch.float32, device=q.device)
         stream = torch.cuda.current_stream()
         sp = stream.cuda_stream
@@ -187,7 +214,11 @@ def main():
         flops = w.flops * (BWD_FLOP_FACTOR if args.backward else 1.0)
 
         def step():
-            if args.backward:
+            if w.dtype == "fp8":
+                st = fa.fa_fwd_fp8(q.data_ptr(), qs.data_ptr(), k.data_ptr(), ks.data_ptr(), v.data_ptr(),
+                                   vs.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H, w.N, w.D, w.causal,
+                                   w.scale, sp)
+            elif args.backward:
                 st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
                                ws.data_ptr(), ws.numel(), w.B, w.H, w.N, w.D, w.causal, w.scale, dt, sp)
@@ -233,8 +264,9 @@ def main():
         tflops = flops / (ms_per_step * 1e-3) / 1e12
         peak = PEAK_TFLOPS[w.dtype]
         achieved = flops / (kernel_ms * 1e-3) / 1e12
-        elt = 2 if w.dtype == "bf16" else 4
-        alg_bytes = w.kv_bytes + 2.0 * w.B * w.H * w.nq * w.D * elt + 4.0 * w.B * w.H * w.nq
+        elt = {"bf16": 2, "fp8": 1}.get(w.dtype, 4)
+        alg_bytes = w.kv_bytes + w.B * w.H * w.nq * w.D * (elt + 2 if w.dtype == "fp8" else 2 * elt) \
+            + 4.0 * w.B * w.H * w.nq + (3.0 * w.B * w.H * w.N * w.D / 32 if w.dtype == "fp8" else 0.0)
         hbm_bound = flops / alg_bytes < peak / PEAK_HBM_GBS * 1e3  # intensity below machine balance
         if hbm_bound:
             roofline = {"bound": "hbm", "achieved": round(alg_bytes / (kernel_ms * 1e-3) / 1e9, 1),
@@ -257,13 +289,15 @@ def main():
             "higher_is_better": True,
             "scaling": "weak",
             "vs_baseline": None,
-            "dtype": w.dtype,
+            "dtype": "fp8_e4m3 (QK^T) + bf16 (PV)" if w.dtype == "fp8" else w.dtype,
             "data": "synthetic: seeded iid N(0,1) inputs"
                     + (" with Q, K x4 (peaked)" if w.variant == fi.PEAKED else "")
-                    + (" rounded to bf16" if w.dtype == "bf16" else ""),
+                    + (" rounded to bf16" if w.dtype == "bf16" else "")
+                    + (" quantised to E4M3 with MX block scales (32 along D)" if w.dtype == "fp8" else ""),
             "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "Nq": w.nq, "D": w.D,
                        "causal": w.causal, "scale": w.scale, "parallelism": "single GPU",
-                       "entry_point": "fa_bwd (dq kernel + dk/dv kernel)" if args.backward else
+                       "entry_point": "fa_fwd_fp8 (E4M3 with MX block scales)" if w.dtype == "fp8" else
+                       "fa_bwd (dq kernel + dk/dv kernel)" if args.backward else
                        "fa_fwd" if split is None else f"fa_fwd_split ({n_ranges} key ranges)",
                        "pct_of_peak": round(100 * tflops / peak, 2),
                        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),

@@ -3,8 +3,9 @@
 Argument marshalling only: every step of the attention runs in the HIP
 kernels of libfa_mi355x.so.  The names mirror the C ABI (fa_fwd, fa_fwd_query,
 fa_fwd_split, fa_fwd_split_query, fa_bwd, fa_bwd_query, fa_status_str,
-fa_abi_version); ``attention_forward``, ``attention_forward_split`` and
-``attention_backward`` are the torch-facing helpers that allocate outputs (and
+fa_fwd_fp8, fa_fwd_fp8_query, fa_abi_version); ``attention_forward``,
+``attention_forward_split``, ``attention_backward`` and ``attention_forward_fp8``
+are the torch-facing helpers that allocate outputs (and
 workspaces) with torch and pass torch's current stream.
 
 The library is loaded on first use; if it has not been built
@@ -37,7 +38,7 @@ FA_SPLIT_AUTO = 0
 FA_SPLIT_MAX = 256
 
 EXPORTED = ("fa_fwd", "fa_fwd_query", "fa_fwd_split", "fa_fwd_split_query", "fa_bwd", "fa_bwd_query",
-            "fa_status_str", "fa_abi_version")
+            "fa_fwd_fp8", "fa_fwd_fp8_query", "fa_status_str", "fa_abi_version")
 
 
 class FaSizes(ctypes.Structure):
@@ -72,6 +73,10 @@ def _load():
                            ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.fa_bwd_query.restype = ctypes.c_int
     lib.fa_bwd_query.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(FaSizes)]
+    lib.fa_fwd_fp8.restype = ctypes.c_int
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp]
+    lib.fa_fwd_fp8_query.restype = ctypes.c_int
+    lib.fa_fwd_fp8_query.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.POINTER(FaSizes)]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_abi_version.restype = ctypes.c_int
@@ -130,6 +135,19 @@ def fa_bwd_query(B, H, N, D, causal, dtype):
     """Returns (status, FaSizes)."""
     sz = FaSizes()
     st = lib().fa_bwd_query(B, H, N, D, int(causal), int(dtype), ctypes.byref(sz))
+    return st, sz
+
+
+def fa_fwd_fp8(q, q_scale, k, k_scale, v, v_scale, o, lse, B, H, N, D, causal, scale, stream) -> int:
+    """Raw C call: pointers as integers (device addresses), returns the fa_status."""
+    return lib().fa_fwd_fp8(q, q_scale, k, k_scale, v, v_scale, o, lse, B, H, N, D, int(causal), float(scale),
+                            stream)
+
+
+def fa_fwd_fp8_query(B, H, N, D, causal):
+    """Returns (status, FaSizes)."""
+    sz = FaSizes()
+    st = lib().fa_fwd_fp8_query(B, H, N, D, int(causal), ctypes.byref(sz))
     return st, sz
 
 
@@ -254,3 +272,35 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
     if st != FA_OK:
         raise FaError(st)
     return dq, dk, dv
+
+
+def attention_forward_fp8(q, q_scale, k, k_scale, v, v_scale, causal: bool = False, scale: float | None = None,
+                          out=None, lse=None, stream=None):
+    """O (bf16), LSE of FP8 inputs with MX block scales, for torch tensors on a GPU.
+
+    q, k, v: contiguous uint8 [B, H, N, D] E4M3 codes; q_scale, k_scale, v_scale:
+    contiguous uint8 [B, H, N, D/32] E8M0 codes.  Launches on ``stream``
+    (default: torch's current stream) and does not synchronise.
+    """
+    import torch
+    B, H, N, D = q.shape
+    for x in (q, k, v):
+        if x.dtype != torch.uint8 or x.shape != q.shape or not x.is_cuda or not x.is_contiguous():
+            raise ValueError("q, k, v must be contiguous uint8 GPU tensors of one shape")
+    for x in (q_scale, k_scale, v_scale):
+        if x.dtype != torch.uint8 or x.shape != (B, H, N, D // 32) or not x.is_cuda or not x.is_contiguous():
+            raise ValueError("scales must be contiguous uint8 GPU tensors [B, H, N, D/32]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_fp8(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(), k_scale.data_ptr(), v.data_ptr(),
+                    v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D, causal, scale,
+                    stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return out, lse

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "fa_check.cpp"), os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_bwd.hip")]
+SOURCES = [os.path.join(CSRC, "fa_check.cpp"), os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_bwd.hip"),
+           os.path.join(CSRC, "fa_fp8.hip")]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled for all device code.

@@ -196,6 +196,42 @@ fa_status check_bwd_call(const void* q, const void* k, const void* v, const void
   return FA_OK;
 }
 
+fa_status check_fp8_shape(int64_t B, int64_t H, int64_t N, int64_t D, fa_sizes* sizes) {
+  fa_sizes sz;
+  fa_status st = check_shape(B, H, N, D, FA_DTYPE_BF16, &sz);  // the bf16 output's limits
+  if (st != FA_OK) return st;
+  const size_t codes = sz.q_bytes / 2;
+  sz.q_bytes = sz.k_bytes = sz.v_bytes = codes;
+  if (sizes) *sizes = sz;
+  return check_supported(B, H, N, D);
+}
+
+fa_status check_fp8_call(const void* q, const void* qs, const void* k, const void* ks, const void* v,
+                         const void* vs, const void* o, const void* lse, int64_t B, int64_t H, int64_t N,
+                         int64_t D, float scale) {
+  if (!q || !qs || !k || !ks || !v || !vs || !o || !lse) return FA_ERR_NULL_POINTER;
+  fa_sizes sz;
+  fa_status st = check_fp8_shape(B, H, N, D, &sz);
+  if (st != FA_OK && st != FA_ERR_UNSUPPORTED) return st;
+  if (!std::isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (st == FA_ERR_UNSUPPORTED) return st;
+  const void* a16[6] = {q, k, v, o, lse, nullptr};
+  for (const void* p : a16)
+    if (p && (uintptr_t)p % 16 != 0) return FA_ERR_MISALIGNED;
+  const void* a4[3] = {qs, ks, vs};
+  for (const void* p : a4)
+    if ((uintptr_t)p % 4 != 0) return FA_ERR_MISALIGNED;
+  const size_t sc_bytes = sz.q_bytes / 32;
+  struct Buf { const void* p; size_t n; };
+  const Buf ins[6] = {{q, sz.q_bytes}, {qs, sc_bytes}, {k, sz.q_bytes}, {ks, sc_bytes}, {v, sz.q_bytes}, {vs, sc_bytes}};
+  const Buf outs[2] = {{o, sz.o_bytes}, {lse, sz.lse_bytes}};
+  if (overlaps(outs[0].p, outs[0].n, outs[1].p, outs[1].n)) return FA_ERR_ALIASING;
+  for (const Buf& ob : outs)
+    for (const Buf& ib : ins)
+      if (overlaps(ob.p, ob.n, ib.p, ib.n)) return FA_ERR_ALIASING;
+  return FA_OK;
+}
+
 }  // namespace fa
 
 extern "C" {

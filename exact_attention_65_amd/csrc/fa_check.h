@@ -46,4 +46,13 @@ fa_status check_bwd_call(const void* q, const void* k, const void* v, const void
                          size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t D, float scale,
                          int dtype);
 
+// fa_fwd_fp8_query: sizes of the E4M3 inputs (1 byte each), the bf16 output
+// and the LSE; no workspace.  The scale arrays hold B*H*N*D/32 bytes each.
+fa_status check_fp8_shape(int64_t B, int64_t H, int64_t N, int64_t D, fa_sizes* sizes);
+
+// Full validation of an fa_fwd_fp8 call, without touching the device.
+fa_status check_fp8_call(const void* q, const void* qs, const void* k, const void* ks, const void* v,
+                         const void* vs, const void* o, const void* lse, int64_t B, int64_t H, int64_t N,
+                         int64_t D, float scale);
+
 }  // namespace fa

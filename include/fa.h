@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 /* Identical to hipStream_t.  NULL means the device's null stream. */
 typedef struct ihipStream_t* fa_stream_t;
@@ -220,6 +220,44 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                  int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale, fa_dtype dtype,
                  fa_stream_t stream);
+
+/*
+ * fa_fwd_fp8_query - buffer sizes of an fa_fwd_fp8 call.
+ *
+ * Pure host function.  q_bytes = k_bytes = v_bytes = B*H*N*D (one byte per
+ * E4M3 code), o_bytes = B*H*N*D*2 (bf16), lse_bytes = B*H*N*4, no workspace.
+ * Each scale array holds B*H*N*(D/32) bytes.  Returns as fa_fwd_query.
+ */
+fa_status fa_fwd_fp8_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, fa_sizes* out);
+
+/*
+ * fa_fwd_fp8 - attention forward on FP8 inputs with MX block scales, enqueued on `stream`.
+ *
+ * q, k, v         : [B, H, N, D] OCP FP8 E4M3 codes (uint8), contiguous.
+ * q_scale, k_scale, v_scale
+ *                 : [B, H, N, D/32] OCP MX E8M0 scale codes (uint8): element
+ *                   (row, d) denotes e4m3(code) * 2^(scale[row][d/32] - 127).
+ *                   V scale codes must lie in 1..254.
+ * o               : [B, H, N, D] bfloat16, written.
+ * lse             : [B, H, N] float32, written (natural log).
+ *
+ * Computes fa_fwd's O and LSE for the values the codes and scales denote.
+ * The pages only name FP8 support and block-scaled attention among the later
+ * FlashAttention versions ("Flash Attention: ускорить attention в 6 раз без
+ * потери точности", sections "Flash Attention 3" and "Flash Attention 4");
+ * the MX format with blocks of 32 along D is this library's reading.  Q K^T
+ * runs on the scaled FP8 matrix instruction (block scales applied by the
+ * hardware, products exact); V is widened to bf16 with its scales (exact) and
+ * P V runs in bf16 with P rounded to bf16, as in fa_fwd.
+ *
+ * q, k, v, o, lse must be 16-byte aligned, the scale arrays 4-byte aligned;
+ * o and lse must not overlap any input or each other (inputs may alias).
+ * Validation and asynchrony as in fa_fwd.  D in {64, 128}; no workspace,
+ * nothing allocated.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* q_scale, const void* k, const void* k_scale, const void* v,
+                     const void* v_scale, void* o, float* lse, int64_t B, int64_t H, int64_t N, int64_t D,
+                     int causal, float scale, fa_stream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);

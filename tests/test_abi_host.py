@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert fa.fa_abi_version() == 3
+    assert fa.fa_abi_version() == 4
     for st in range(10):
         s = fa.fa_status_str(st)
         assert s.startswith("FA_")
@@ -144,8 +144,8 @@ def test_every_kernel_stub_is_defined():
     undefined = [l for l in out.splitlines() if " U " in l and "_ZN2fa" in l]
     assert undefined == []
     kernels = set(re.findall(r"(_ZN2fa\d+fa_\w+_kernelI\w+)", out))
-    # bf16: D x causal x split; fp32: D x causal; merge: D; backward: 2 kernels x D x causal
-    assert len(kernels) == 8 + 4 + 2 + 8, kernels
+    # bf16: D x causal x split; fp32: D x causal; merge: D; backward: 2 kernels x D x causal; fp8: D x causal
+    assert len(kernels) == 8 + 4 + 2 + 8 + 4, kernels
 
 
 # ---------------------------------------------------------------- fa_fwd_split
@@ -271,3 +271,41 @@ def test_bwd_validation_before_any_device_call(kw, expect):
     if expect == fa.FA_ERR_HIP and gpu_visible():
         pytest.skip("valid arguments would launch on fake addresses when a GPU is visible")
     assert bwd_call(**kw) == expect
+
+
+# ---------------------------------------------------------------- fa_fwd_fp8
+def test_fp8_query_sizes():
+    st, sz = fa.fa_fwd_fp8_query(2, 32, 4096, 128, 0)
+    assert st == fa.FA_OK
+    assert sz.q_bytes == sz.k_bytes == sz.v_bytes == 2 * 32 * 4096 * 128
+    assert sz.o_bytes == 2 * sz.q_bytes and sz.lse_bytes == 2 * 32 * 4096 * 4 and sz.workspace_bytes == 0
+    assert fa.fa_fwd_fp8_query(1, 1, 64, 96, 0)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_fp8_query(1, 1, 0, 64, 0)[0] == fa.FA_ERR_BAD_SHAPE
+    assert fa.lib().fa_fwd_fp8_query(1, 1, 64, 64, 0, None) == fa.FA_ERR_NULL_POINTER
+
+
+def fp8_call(q=A, qs=A + SZ, k=A + 2 * SZ, ks=A + 3 * SZ, v=A + 4 * SZ, vs=A + 5 * SZ, o=A + 6 * SZ,
+             lse=A + 7 * SZ, B=1, H=2, N=100, D=64, causal=0, scale=0.125):
+    return fa.fa_fwd_fp8(q, qs, k, ks, v, vs, o, lse, B, H, N, D, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), fa.FA_ERR_HIP),                                # valid: fails only at the device query
+    (dict(k=A, v=A, ks=A + SZ, vs=A + SZ), fa.FA_ERR_HIP),  # inputs may alias
+    (dict(qs=0), fa.FA_ERR_NULL_POINTER),
+    (dict(lse=0), fa.FA_ERR_NULL_POINTER),
+    (dict(q=A + 8), fa.FA_ERR_MISALIGNED),
+    (dict(vs=A + 5 * SZ + 2), fa.FA_ERR_MISALIGNED),
+    (dict(vs=A + 5 * SZ + 4), fa.FA_ERR_HIP),               # scales need only 4-byte alignment
+    (dict(o=A + 5 * SZ), fa.FA_ERR_ALIASING),               # o on top of v's scales
+    (dict(lse=A + 6 * SZ + 16), fa.FA_ERR_ALIASING),        # lse inside o
+    (dict(o=A + 4 * SZ + 100 * 64 * 2 - 16), fa.FA_ERR_ALIASING),  # o starts in v's last 16 bytes
+    (dict(o=A + 4 * SZ + 100 * 64 * 2), fa.FA_ERR_HIP),     # o right after v: valid
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=-1), fa.FA_ERR_BAD_SHAPE),
+])
+def test_fp8_validation_before_any_device_call(kw, expect):
+    if expect == fa.FA_ERR_HIP and gpu_visible():
+        pytest.skip("valid arguments would launch on fake addresses when a GPU is visible")
+    assert fp8_call(**kw) == expect

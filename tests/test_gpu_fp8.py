@@ -1,0 +1,155 @@
+"""fa_fwd_fp8 against the fp64 oracle of the dequantised inputs
+(oracle.attention_fp8_ref).
+
+Tolerance: the bf16 contract (max |dO| <= 2e-2, mean |dO| <= 2e-3, |dLSE| <=
+1e-3), because the roundings left are those of fa_fwd: V is widened to bf16
+exactly and P and O are rounded to bf16.  One more source: the scaled FP8
+matrix instruction does not sum its products at full fp32 precision (measured
+on the device: errors of about 2e-5, at most 1.7e-4, of the sum of the
+products' magnitudes), so score errors grow with the scores; as for fp32
+inputs, the LSE bound is scaled by max(1, max|score| / 5).  The generator's
+inputs dequantise to values of unit scale like the bf16 workloads'; inputs
+with larger values get the O bounds scaled by their RMS.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_65_amd as fa
+import fa_inputs as fi
+import fa_inputs.fp8 as f8
+from oracle import attention_fp8_ref, attention_ref, mx_dequantize
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _inputs(w):
+    return [f8.full_mx(w, t) for t in (fi.T_Q, fi.T_K, fi.T_V)]
+
+
+def _run(inp, causal, scale, out=None, lse=None):
+    (q, qs), (k, ks), (v, vs) = inp
+    o, l = fa.attention_forward_fp8(_dev(q), _dev(qs), _dev(k), _dev(ks), _dev(v), _dev(vs), causal=causal,
+                                    scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o, l
+
+
+def _compare(inp, o, lse, heads, causal, scale, what, rows_for=None):
+    (q, qs), (k, ks), (v, vs) = inp
+    worst = dict(o_max=0.0, o_mean=0.0, lse_max=0.0, finite=True)
+    n_el, acc = 0, 0.0
+    vrms, sratio = 1.0, 1.0
+    for b, h in heads:
+        rows = None if rows_for is None else rows_for(h)
+        o_ref, lse_ref = attention_fp8_ref(q[b, h], qs[b, h], k[b, h], ks[b, h], v[b, h], vs[b, h], causal, scale,
+                                           rows=rows)
+        vrms = max(vrms, float(np.sqrt(np.mean(mx_dequantize(v[b, h], vs[b, h]) ** 2))))
+        sratio = max(sratio, gu.score_ratio(mx_dequantize(q[b, h], qs[b, h]), mx_dequantize(k[b, h], ks[b, h]),
+                                            scale, causal))
+        og = o[b, h].float().cpu().numpy()
+        lg = lse[b, h].cpu().numpy()
+        if rows is not None:
+            og, lg = og[rows], lg[rows]
+        e = gu.errors(og, lg, o_ref, lse_ref)
+        worst["o_max"] = max(worst["o_max"], e["o_max"])
+        worst["lse_max"] = max(worst["lse_max"], e["lse_max"])
+        worst["finite"] &= e["finite"]
+        acc += e["o_mean"] * o_ref.size
+        n_el += o_ref.size
+    worst["o_mean"] = acc / n_el
+    if vrms > 1.0:
+        worst = dict(worst, o_max=worst["o_max"] / vrms, o_mean=worst["o_mean"] / vrms)
+    if sratio > 1.0:
+        worst = dict(worst, lse_max=worst["lse_max"] / sratio)
+    gu.assert_within(worst, "bf16", what + (f" (O errors / V rms {vrms:.1f})" if vrms > 1.0 else "")
+                     + (f" (LSE error / score ratio {sratio:.1f})" if sratio > 1.0 else ""))
+
+
+SMALL_N = [1, 17, 64, 65, 128, 129, 200, 333, 1000]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", SMALL_N)
+def test_fp8_small_shapes(N, causal, D):
+    w = fi.Workload(f"fp8_n{N}_d{D}", 800 + 4 * SMALL_N.index(N) + D // 64, 1, 2, N, D, "fp8", causal)
+    gu.log(f"[gpu] fp8 N={N} D={D} causal={causal}")
+    inp = _inputs(w)
+    o, lse = _run(inp, causal, w.scale)
+    _compare(inp, o, lse, [(0, 0), (0, 1)], causal, w.scale, f"{w.name} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.3])
+def test_fp8_other_scales(scale):
+    w = fi.Workload("fp8_scale_n300_d128", 850, 1, 2, 300, 128, "fp8", True)
+    inp = _inputs(w)
+    o, lse = _run(inp, True, scale)
+    _compare(inp, o, lse, [(0, 0), (0, 1)], True, scale, f"{w.name} scale={scale}")
+
+
+def test_fp8_block_scales_vary():
+    """Scale codes drawn independently per block over a wide range: every
+    block's scale must reach the right products."""
+    w = fi.Workload("fp8_wide_n257_d128", 851, 1, 2, 257, 128, "fp8", False)
+    inp = _inputs(w)
+    g = np.random.default_rng(851)
+    # Q, K block scales over 2^-12 .. 2^-4 (scores of order one at scale 2^-7),
+    # V block scales over 2^-17 .. 2^6 (O errors are judged relative to V's RMS)
+    ranges = ((115, 124), (115, 124), (110, 134))
+    out = [(codes, g.integers(lo, hi, sc.shape).astype(np.uint8)) for (codes, sc), (lo, hi) in zip(inp, ranges)]
+    o, lse = _run(out, False, 2.0 ** -7)
+    # V values span 2^23 here, so no single absolute bound fits every output;
+    # each element is bounded by the bf16 error model instead: the weights are
+    # normalised by their own rounded sum, so each carries at most 2 * 2^-9
+    # relative error, and O is rounded once more: |dO| <= 2^-8 (W|V|) + 2^-9 |O|
+    # (bounds doubled for margin)
+    (q, qs), (k, ks), (v, vs) = out
+    for hh in range(2):
+        qd, kd, vd = (mx_dequantize(c[0, hh], sc[0, hh]) for c, sc in out)
+        o_ref, lse_ref = attention_ref(qd, kd, vd, False, 2.0 ** -7)
+        wabs, _ = attention_ref(qd, kd, np.abs(vd), False, 2.0 ** -7)
+        err = np.abs(o[0, hh].float().cpu().numpy() - o_ref)
+        bound = 2.0 ** -7 * wabs + 2.0 ** -8 * np.abs(o_ref) + 1e-30
+        ratio = float((err / bound).max())
+        gu.log(f"  {w.name} head {hh}: max |dO| / bound = {ratio:.3f}, "
+               f"max|dLSE| = {np.abs(lse[0, hh].cpu().numpy() - lse_ref).max():.2e}")
+        assert ratio <= 1.0, f"{w.name} head {hh}: error above the bf16 error-model bound ({ratio:.3f})"
+        assert np.abs(lse[0, hh].cpu().numpy() - lse_ref).max() <= 1e-3
+
+
+def test_fp8_peaked_scores():
+    w = fi.Workload("fp8_peaked_n512_d128", 852, 1, 4, 512, 128, "fp8", True, fi.PEAKED)
+    inp = _inputs(w)
+    o, lse = _run(inp, True, w.scale)
+    _compare(inp, o, lse, [(0, h) for h in range(4)], True, w.scale, w.name)
+
+
+def test_fp8_outputs_written_and_deterministic():
+    w = fi.Workload("fp8_canary_n999_d128", 853, 2, 3, 999, 128, "fp8", True)
+    inp = _inputs(w)
+    runs = []
+    for _ in range(2):
+        o = torch.full((2, 3, 999, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((2, 3, 999), float("nan"), device="cuda")
+        _run(inp, True, w.scale, out=o, lse=lse)
+        assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+        runs.append((o.clone(), lse.clone()))
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+
+
+def test_fp8_full_size_workload():
+    """The FP8 headline-shape workload in the benchmark's launch configuration:
+    two seeded heads on every row, every head on seeded rows."""
+    w = fi.FP8_N4096
+    gu.log(f"[gpu] fp8 workload {w.name}")
+    inp = _inputs(w)
+    o, lse = _run(inp, w.causal, w.scale)
+    _compare(inp, o, lse, fi.sample_heads(w, 2), w.causal, w.scale, w.name + " full heads")
+    _compare(inp, o, lse, [(b, h) for b in range(w.B) for h in range(w.H)], w.causal, w.scale,
+             w.name + " sampled rows", rows_for=lambda h: fi.sample_rows(w, h, 32))

@@ -88,3 +88,20 @@ def test_backward_tile_barriers_drain_vmcnt(bwd_asm):
 def test_backward_kernels_do_not_spill(bwd_asm):
     for m in re.finditer(r"\.name:\s+(_ZN2fa\w*bwd\w*)\s.*?\.vgpr_spill_count:\s+(\d+)", bwd_asm, re.S):
         assert int(m.group(2)) == 0, m.group(1)
+
+
+@pytest.fixture(scope="module")
+def fp8_asm() -> str:
+    return fabuild.device_asm("fa_fp8.hip")
+
+
+def test_fp8_kernels_barriers_drain_vmcnt_and_do_not_spill(fp8_asm):
+    kernels = _kernels(fp8_asm)
+    assert sum("fp8_kernel" in n for n, _ in kernels) == 4, [n for n, _ in kernels]
+    for name, body in kernels:
+        waits = _barrier_waits(body)
+        assert waits, f"{name}: no barrier after a tile load"
+        bad = [i for i, ok in waits if not ok]
+        assert not bad, f"{name}: barrier(s) at asm line(s) {bad} do not wait for the LDS tile loads"
+    for m in re.finditer(r"\.name:\s+(_ZN2fa\w*fp8\w*)\s.*?\.vgpr_spill_count:\s+(\d+)", fp8_asm, re.S):
+        assert int(m.group(2)) == 0, m.group(1)
