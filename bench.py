@@ -46,7 +46,7 @@ HEADLINE = "bf16_b2_h32_n4096_d128"
 # The FP8 path runs Q K^T on the fp8 matrix cores and P V on the bf16 ones, half of the FLOPs each:
 # its ceiling is the harmonic combination of the two peaks.
 PEAK_FP8_MIXED = 1.0 / (0.5 / 5033.2 + 0.5 / 2516.6)
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": PEAK_FP8_MIXED}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "fp8": PEAK_FP8_MIXED}
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 KERNEL_SOURCES = ["exact_attention_65_amd/csrc/fa_fwd_kernel.hpp", "exact_attention_65_amd/csrc/fa_fwd.hip"]
 BWD_FLOP_FACTOR = 2.5  # five N x N x D products against the forward's two
@@ -157,7 +157,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    names = [w.name for w in fi.ALL_WORKLOADS + fi.SPLIT_WORKLOADS + fi.FP8_WORKLOADS] if args.sweep \
+    names = [w.name for w in fi.ALL_WORKLOADS + fi.SPLIT_WORKLOADS + fi.FP8_WORKLOADS + fi.F16_WORKLOADS] \
+        if args.sweep \
         else [args.workload]
     for name in names:
         w = fi.workload_by_name(name)
@@ -168,9 +169,9 @@ def main():
                 continue
         if w.dtype == "fp8":
             split = None
-        if split is not None and w.dtype != "bf16":
+        if split is not None and w.dtype not in ("bf16", "f16"):
             continue
-        dt = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32
+        dt = {"bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16}.get(w.dtype, fa.FA_DTYPE_F32)
         tensors = []
         if w.dtype == "fp8":
             import fa_inputs.fp8 as f8
@@ -186,7 +187,7 @@ def main():
             for t in (fi.T_Q, fi.T_K, fi.T_V):
                 bits = fi.full_tensor(w, t)
                 x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" \
-                    else torch.from_numpy(bits)
+                    else torch.from_numpy(bits.view(np.float16)) if w.dtype == "f16" else torch.from_numpy(bits)
                 tensors.append(x.cuda())
                 del bits, x
             q, k, v = tensors
@@ -264,7 +265,7 @@ def main():
         tflops = flops / (ms_per_step * 1e-3) / 1e12
         peak = PEAK_TFLOPS[w.dtype]
         achieved = flops / (kernel_ms * 1e-3) / 1e12
-        elt = {"bf16": 2, "fp8": 1}.get(w.dtype, 4)
+        elt = {"bf16": 2, "f16": 2, "fp8": 1}.get(w.dtype, 4)
         alg_bytes = w.kv_bytes + w.B * w.H * w.nq * w.D * (elt + 2 if w.dtype == "fp8" else 2 * elt) \
             + 4.0 * w.B * w.H * w.nq + (3.0 * w.B * w.H * w.N * w.D / 32 if w.dtype == "fp8" else 0.0)
         hbm_bound = flops / alg_bytes < peak / PEAK_HBM_GBS * 1e3  # intensity below machine balance
@@ -293,6 +294,7 @@ def main():
             "data": "synthetic: seeded iid N(0,1) inputs"
                     + (" with Q, K x4 (peaked)" if w.variant == fi.PEAKED else "")
                     + (" rounded to bf16" if w.dtype == "bf16" else "")
+                    + (" rounded to fp16" if w.dtype == "f16" else "")
                     + (" quantised to E4M3 with MX block scales (32 along D)" if w.dtype == "fp8" else ""),
             "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "Nq": w.nq, "D": w.D,
                        "causal": w.causal, "scale": w.scale, "parallelism": "single GPU",

@@ -22,6 +22,7 @@ from .build import LIB_PATH
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
+FA_DTYPE_F16 = 2
 
 FA_OK = 0
 FA_ERR_NULL_POINTER = 1
@@ -159,21 +160,24 @@ def fa_abi_version() -> int:
     return lib().fa_abi_version()
 
 
+def _dtype_code(dtype) -> int:
+    import torch
+    codes = {torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_F16, torch.float32: FA_DTYPE_F32}
+    if dtype not in codes:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return codes[dtype]
+
+
 def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
                       out=None, lse=None, stream=None):
     """O, LSE = attention(q, k, v) for torch tensors [B, H, N, D] on a GPU.
 
-    q, k, v: contiguous, same shape, dtype torch.bfloat16 or torch.float32.
-    Returns (o, lse): o like q, lse float32 [B, H, N].  Launches on ``stream``
-    (default: torch's current stream) and does not synchronise.
+    q, k, v: contiguous, same shape, dtype torch.bfloat16, torch.float16 or
+    torch.float32.  Returns (o, lse): o like q, lse float32 [B, H, N].  Launches
+    on ``stream`` (default: torch's current stream) and does not synchronise.
     """
     import torch
-    if q.dtype == torch.bfloat16:
-        dt = FA_DTYPE_BF16
-    elif q.dtype == torch.float32:
-        dt = FA_DTYPE_F32
-    else:
-        raise TypeError(f"unsupported dtype {q.dtype}")
+    dt = _dtype_code(q.dtype)
     for x in (q, k, v):
         if x.dtype != q.dtype or x.shape != q.shape or not x.is_cuda or not x.is_contiguous():
             raise ValueError("q, k, v must be contiguous GPU tensors of one shape and dtype")
@@ -195,7 +199,7 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
 
 def attention_forward_split(q, k, v, causal: bool = False, scale: float | None = None,
                             n_splits: int = FA_SPLIT_AUTO, out=None, lse=None, workspace=None, stream=None):
-    """O, LSE = attention(q, k, v) through fa_fwd_split, for bf16 torch tensors.
+    """O, LSE = attention(q, k, v) through fa_fwd_split, for bf16 or fp16 torch tensors.
 
     q: [B, H, Nq, D], k and v: [B, H, Nk, D] (contiguous, one dtype, on a GPU).
     Under the causal mask the queries are the last Nq positions (Nq <= Nk).
@@ -203,7 +207,8 @@ def attention_forward_split(q, k, v, causal: bool = False, scale: float | None =
     Launches on ``stream`` (default: torch's current stream); no synchronisation.
     """
     import torch
-    if q.dtype != torch.bfloat16:
+    dt = _dtype_code(q.dtype)
+    if dt == FA_DTYPE_F32:
         raise TypeError(f"unsupported dtype {q.dtype}")
     for x in (q, k, v):
         if x.dtype != q.dtype or not x.is_cuda or not x.is_contiguous() or x.dim() != 4:
@@ -214,7 +219,7 @@ def attention_forward_split(q, k, v, causal: bool = False, scale: float | None =
         raise ValueError("k and v must be [B, H, Nk, D] with q's B, H, D")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    st, sz, splits = fa_fwd_split_query(B, H, Nq, Nk, D, causal, n_splits, FA_DTYPE_BF16)
+    st, sz, splits = fa_fwd_split_query(B, H, Nq, Nk, D, causal, n_splits, dt)
     if st != FA_OK:
         raise FaError(st)
     if out is None:
@@ -228,7 +233,7 @@ def attention_forward_split(q, k, v, causal: bool = False, scale: float | None =
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
-                      B, H, Nq, Nk, D, causal, scale, n_splits, FA_DTYPE_BF16, stream.cuda_stream)
+                      B, H, Nq, Nk, D, causal, scale, n_splits, dt, stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st)
     return out, lse

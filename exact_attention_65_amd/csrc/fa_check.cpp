@@ -10,6 +10,7 @@ size_t elem_size(int dtype) {
   switch (dtype) {
     case FA_DTYPE_F32: return 4;
     case FA_DTYPE_BF16: return 2;
+    case FA_DTYPE_F16: return 2;
     default: return 0;
   }
 }
@@ -105,7 +106,7 @@ fa_status check_split_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_
   if (qbytes > (uint64_t)SIZE_MAX || kbytes > (uint64_t)SIZE_MAX) return FA_ERR_BAD_SHAPE;
   // the arguments are valid; what follows decides whether the kernels support them
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
   if (Nq * D > (int64_t)INT32_MAX || Nk * D > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
   const int64_t qblocks = (Nq + kRowsPerBlock - 1) / kRowsPerBlock;
   if (B > kMaxGrid / H || B * H > kMaxGrid / qblocks) return FA_ERR_UNSUPPORTED;
@@ -267,7 +268,7 @@ __attribute__((visibility("default"))) const char* fa_status_str(fa_status s) {
     case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a required pointer is NULL";
     case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: B, H, N, D must be positive and sizes must fit size_t";
     case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE: scale must be finite";
-    case FA_ERR_BAD_DTYPE: return "FA_ERR_BAD_DTYPE: dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16";
+    case FA_ERR_BAD_DTYPE: return "FA_ERR_BAD_DTYPE: dtype must be FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16";
     case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: every pointer must be 16-byte aligned";
     case FA_ERR_ALIASING: return "FA_ERR_ALIASING: outputs and workspace must not overlap the inputs or each other";
     case FA_ERR_UNSUPPORTED:

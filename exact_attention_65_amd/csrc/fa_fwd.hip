@@ -48,10 +48,17 @@ hipError_t launch(Kern kern, int blocks, const FwdArgs& a, int threads, hipStrea
   return hipGetLastError();
 }
 
-// bf16 attention kernel for (D, causal, split); 256 threads, 128 query rows
+// 16-bit (bf16 or fp16) attention kernel for (D, causal, split); 256 threads,
+// 128 query rows
 template <bool SPLIT>
-hipError_t launch_bf16(int D, bool causal, const FwdArgs& a, hipStream_t s) {
+hipError_t launch_h16(int dtype, int D, bool causal, const FwdArgs& a, hipStream_t s) {
   const int t = kBF16Threads, n = a.n_blocks;
+  if (dtype == FA_DTYPE_F16) {
+    if (D == 128) return causal ? launch(fa_fwd_f16_kernel<128, true, SPLIT>, n, a, t, s)
+                                : launch(fa_fwd_f16_kernel<128, false, SPLIT>, n, a, t, s);
+    return causal ? launch(fa_fwd_f16_kernel<64, true, SPLIT>, n, a, t, s)
+                  : launch(fa_fwd_f16_kernel<64, false, SPLIT>, n, a, t, s);
+  }
   if (D == 128) return causal ? launch(fa_fwd_bf16_kernel<128, true, SPLIT>, n, a, t, s)
                               : launch(fa_fwd_bf16_kernel<128, false, SPLIT>, n, a, t, s);
   return causal ? launch(fa_fwd_bf16_kernel<64, true, SPLIT>, n, a, t, s)
@@ -68,10 +75,13 @@ hipError_t launch_f32(int D, bool causal, const FwdArgs& a, hipStream_t s) {
 }
 
 // merge of the key ranges: one lane group per output row
-hipError_t launch_combine(int D, const FwdArgs& a, hipStream_t s) {
+hipError_t launch_combine(int dtype, int D, const FwdArgs& a, hipStream_t s) {
   const long long rows = (long long)a.n_bh * a.nq;
   const int per_block = kCombineThreads / (D / 8);
   const int blocks = (int)((rows + per_block - 1) / per_block);
+  if (dtype == FA_DTYPE_F16)
+    return D == 128 ? launch(fa_combine_f16_kernel<128>, blocks, a, kCombineThreads, s)
+                    : launch(fa_combine_f16_kernel<64>, blocks, a, kCombineThreads, s);
   if (D == 128) return launch(fa_combine_kernel<128>, blocks, a, kCombineThreads, s);
   return launch(fa_combine_kernel<64>, blocks, a, kCombineThreads, s);
 }
@@ -95,7 +105,7 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* o, float* l
   const float c = std::fabs(scale) * 1.44269504088896340736f;
   a.c = c < FLT_MIN ? FLT_MIN : c;
   a.qflip = 0u;
-  if (std::signbit(scale) && scale != 0.0f) a.qflip = dtype == FA_DTYPE_BF16 ? 0x80008000u : 0x80000000u;
+  if (std::signbit(scale) && scale != 0.0f) a.qflip = dtype == FA_DTYPE_F32 ? 0x80000000u : 0x80008000u;
   a.o_part = nullptr;
   a.lse_part = nullptr;
   return a;
@@ -119,12 +129,12 @@ extern "C" __attribute__((visibility("default"))) fa_status fa_fwd(
   if (st != FA_OK) return st;
   if ((st = fa::device_check()) != FA_OK) return st;
 
-  const bool bf16 = dtype == FA_DTYPE_BF16;
+  const bool h16 = dtype != FA_DTYPE_F32;
   const fa::FwdArgs a =
-      fa::make_args(q, k, v, o, lse, B, H, N, N, scale, (int)dtype, bf16 ? fa::kBF16Rows : fa::kBM, 1);
+      fa::make_args(q, k, v, o, lse, B, H, N, N, scale, (int)dtype, h16 ? fa::kBF16Rows : fa::kBM, 1);
   const hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = bf16 ? fa::launch_bf16<false>((int)D, causal != 0, a, s)
-                            : fa::launch_f32((int)D, causal != 0, a, s);
+  const hipError_t e = h16 ? fa::launch_h16<false>((int)dtype, (int)D, causal != 0, a, s)
+                           : fa::launch_f32((int)D, causal != 0, a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -140,10 +150,11 @@ extern "C" __attribute__((visibility("default"))) fa_status fa_fwd_split(
 
   fa::FwdArgs a = fa::make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, (int)dtype, fa::kBF16Rows, splits);
   const hipStream_t s = (hipStream_t)stream;
-  if (splits == 1) return fa::launch_bf16<false>((int)D, causal != 0, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  if (splits == 1)
+    return fa::launch_h16<false>((int)dtype, (int)D, causal != 0, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
   // workspace: [splits][B*H][Nq][D] float outputs, then [splits][B*H][Nq] log-sum-exps
   a.o_part = (float*)workspace;
   a.lse_part = a.o_part + (size_t)splits * a.n_bh * a.nq * D;
-  if (fa::launch_bf16<true>((int)D, causal != 0, a, s) != hipSuccess) return FA_ERR_HIP;
-  return fa::launch_combine((int)D, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  if (fa::launch_h16<true>((int)dtype, (int)D, causal != 0, a, s) != hipSuccess) return FA_ERR_HIP;
+  return fa::launch_combine((int)dtype, (int)D, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -101,6 +101,43 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f16x2 v;
+  v[0] = (_Float16)lo;
+  v[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// The 16-bit element types of the MFMA kernels: the 8-element operand vector,
+// two fp32 values rounded (to nearest even) into one word, the 32x32x16 MFMA
+// with fp32 accumulation, and the sum of the two elements of a word added to
+// an fp32 accumulator (a dot product with (1, 1)).
+struct BF16 {
+  typedef bf16x8 vec8;
+  __device__ static __forceinline__ uint32_t pack(float lo, float hi) { return pack_bf16(lo, hi); }
+  __device__ static __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float sum2(uint32_t w, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+  }
+};
+struct F16 {
+  typedef f16x8 vec8;
+  __device__ static __forceinline__ uint32_t pack(float lo, float hi) { return pack_f16(lo, hi); }
+  __device__ static __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float sum2(uint32_t w, float acc) {
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), ones, acc, false);
+  }
+};
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 // Pins a value in place: the empty asm "reads and rewrites" it, so its
@@ -224,8 +261,12 @@ constexpr int kBF16Rows = 128;
 // normalised fp32 output and log-sum-exp over its range to o_part / lse_part,
 // and fa_combine_kernel merges them.  Without SPLIT the one workgroup of a query
 // block covers all its keys and writes O and LSE.
-template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
+//
+// The body serves both 16-bit input types (E = BF16 or F16): the kernels
+// fa_fwd_bf16_kernel and fa_fwd_f16_kernel below instantiate it.
+template <typename E, int D, bool CAUSAL, bool SPLIT>
+__device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
+  typedef typename E::vec8 vec8;
   constexpr int BN = 64;                // keys per tile
   constexpr int RB = D * 2;             // bytes per K / V row
   constexpr int CPR = D / 8;            // 16-byte chunks per row
@@ -297,14 +338,14 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
 
   // Q fragments: B operand of the score MFMA, Q[qrow][16kk + 8h .. +7] (signs
   // flipped for a negative scale)
-  bf16x8 qf[NKK];
+  vec8 qf[NKK];
   {
     const u32x4 flip = {a.qflip, a.qflip, a.qflip, a.qflip};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (qrow < NQ) x = *(const u32x4*)(Qg + (size_t)qrow * D + 16 * kk + 8 * h) ^ flip;
-      qf[kk] = __builtin_bit_cast(bf16x8, x);
+      qf[kk] = __builtin_bit_cast(vec8, x);
     }
   }
 
@@ -363,12 +404,11 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
   f32x16 sA[NKB], sB[NKB];
-  bf16x8 pf[NCC];
+  vec8 pf[NCC];
   float m_ref = neg_inf(), l = 0.0f, lx = 0.0f, mu = 0.0f;
   bool pend = false;
   float pend_alpha = 1.0f;
   const float c = a.c;
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // ---- pieces of the softmax -------------------------------------------
   // mask keys past the workgroup's key range (past NK, or in the next
@@ -430,10 +470,10 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
     for (int e = 0; e < 4; ++e) s[kb][base + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][base + e], c, -mu));
     // each packed word is a scalar before it is bit-cast: this compiler
     // miscompiles __builtin_bit_cast applied to an element of a vector variable
-    const uint32_t w0 = pack_bf16(s[kb][base + 0], s[kb][base + 1]);
-    const uint32_t w1 = pack_bf16(s[kb][base + 2], s[kb][base + 3]);
-    lsum[half] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, lsum[half], false);
-    lsum[half] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, lsum[half], false);
+    const uint32_t w0 = E::pack(s[kb][base + 0], s[kb][base + 1]);
+    const uint32_t w1 = E::pack(s[kb][base + 2], s[kb][base + 3]);
+    lsum[half] = E::sum2(w0, lsum[half]);
+    lsum[half] = E::sum2(w1, lsum[half]);
     xsum[half] += s[kb][base + 0] + s[kb][base + 1];
     xsum[half] += s[kb][base + 2] + s[kb][base + 3];
     uint32_t r0 = w0, r1 = w1;
@@ -470,15 +510,14 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
       if (k < NSA) {
         const int kk = k / NKB, kb = k % NKB;
         const f32x16 z = {};
-        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[k]), qf[kk],
-                                                         kk == 0 ? z : sn[kb], 0, 0, 0);
+        sn[kb] = E::mfma(__builtin_bit_cast(vec8, kf[k]), qf[kk], kk == 0 ? z : sn[kb]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
       const u32x4 x = {pw[2 * cc][0], pw[2 * cc][1], pw[2 * cc + 1][0], pw[2 * cc + 1][1]};
-      pf[cc] = __builtin_bit_cast(bf16x8, x);
+      pf[cc] = __builtin_bit_cast(vec8, x);
     }
     l += lsum[0] + lsum[1];
     lx += xsum[0] + xsum[1];
@@ -494,7 +533,7 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
       // well before the next phase needs mu
       if (k <= NKB) ref_slice(sn, k);
       const int db = k % NDB, cc = k / NDB;
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[k]), pf[cc], o[db], 0, 0, 0);
+      o[db] = E::mfma(__builtin_bit_cast(vec8, vf[k]), pf[cc], o[db]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -522,8 +561,7 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
     for (int k = 0; k < NSA; ++k) {
       const int kk = k / NKB, kb = k % NKB;
       const f32x16 z = {};
-      sA[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kfrag(kA, k)), qf[kk],
-                                                       kk == 0 ? z : sA[kb], 0, 0, 0);
+      sA[kb] = E::mfma(__builtin_bit_cast(vec8, kfrag(kA, k)), qf[kk], kk == 0 ? z : sA[kb]);
     }
     mask(sA, t_lo);
 #pragma unroll
@@ -589,13 +627,22 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = 32 * db + 8 * g + 4 * h;
-          const u32x2 w = {pack_bf16(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
-                           pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+          const u32x2 w = {E::pack(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
+                           E::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
           *(u32x2*)(Og + d) = w;
         }
       if (h == 0) a.lse[(size_t)bh * NQ + qrow] = lse_row;
     }
   }
+}
+
+template <int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
+  fwd16_body<BF16, D, CAUSAL, SPLIT>(a);
+}
+template <int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_f16_kernel(FwdArgs a) {
+  fwd16_body<F16, D, CAUSAL, SPLIT>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -605,11 +652,12 @@ __global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a)
 // section "Lösung: Online Softmax") applied to the summaries of whole key
 // ranges, with the largest lse_s subtracted before exponentiating.  Ranges in
 // which a row sees no key (lse_s = -inf) add nothing.  Each group of D/8 lanes
-// handles one row, 8 output elements per lane; O is rounded to bf16 once.
+// handles one row, 8 output elements per lane; O is rounded to the output's
+// 16-bit type once.
 constexpr int kCombineThreads = 256;
 
-template <int D>
-__global__ __launch_bounds__(kCombineThreads) void fa_combine_kernel(FwdArgs a) {
+template <typename E, int D>
+__device__ __forceinline__ void combine_body(const FwdArgs& a) {
   constexpr int TPR = D / 8;                       // lanes per row
   constexpr int RPB = kCombineThreads / TPR;       // rows per workgroup
   const int tid = threadIdx.x;
@@ -636,10 +684,19 @@ __global__ __launch_bounds__(kCombineThreads) void fa_combine_kernel(FwdArgs a) 
     }
   }
   const float inv = 1.0f / tot;
-  const u32x4 w = {pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv),
-                   pack_bf16(acc[4] * inv, acc[5] * inv), pack_bf16(acc[6] * inv, acc[7] * inv)};
+  const u32x4 w = {E::pack(acc[0] * inv, acc[1] * inv), E::pack(acc[2] * inv, acc[3] * inv),
+                   E::pack(acc[4] * inv, acc[5] * inv), E::pack(acc[6] * inv, acc[7] * inv)};
   *(u32x4*)((uint16_t*)a.o + row * D + d0) = w;
   if (d0 == 0) a.lse[row] = m + __logf(tot);
+}
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void fa_combine_kernel(FwdArgs a) {
+  combine_body<BF16, D>(a);
+}
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void fa_combine_f16_kernel(FwdArgs a) {
+  combine_body<F16, D>(a);
 }
 
 // ---------------------------------------------------------------------------

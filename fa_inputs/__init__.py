@@ -45,7 +45,7 @@ class Workload:
     H: int
     N: int
     D: int
-    dtype: str  # "f32", "bf16" or "fp8" (E4M3 codes with MX block scales: fa_inputs.fp8)
+    dtype: str  # "f32", "bf16", "f16" or "fp8" (E4M3 codes with MX block scales: fa_inputs.fp8)
     causal: bool
     variant: int = PLAIN
     NQ: int = 0  # query rows per head; 0: as many as keys (N)
@@ -73,7 +73,7 @@ class Workload:
     @property
     def kv_bytes(self) -> float:
         """Bytes of K and V (the stream a decode step is bound by)."""
-        return 2.0 * self.B * self.H * self.N * self.D * {"bf16": 2, "fp8": 1}.get(self.dtype, 4)
+        return 2.0 * self.B * self.H * self.N * self.D * {"bf16": 2, "f16": 2, "fp8": 1}.get(self.dtype, 4)
 
     def rows(self, t: int) -> int:
         """Rows of tensor t in one head: nq for Q and dO, N for K and V."""
@@ -109,10 +109,13 @@ SPLIT_WORKLOADS = (SPLIT_DECODE, SPLIT_CHUNK)
 # quantised to E4M3 with MX block scales (fa_inputs.fp8).
 FP8_N4096 = Workload("fp8_b2_h32_n4096_d128", 6, 2, 32, 4096, 128, "fp8", False)
 FP8_WORKLOADS = (FP8_N4096,)
+# fp16 inputs at the headline shape
+F16_N4096 = Workload("f16_b2_h32_n4096_d128", 7, 2, 32, 4096, 128, "f16", False)
+F16_WORKLOADS = (F16_N4096,)
 
 
 def workload_by_name(name: str) -> Workload:
-    for w in ALL_WORKLOADS + SPLIT_WORKLOADS + FP8_WORKLOADS:
+    for w in ALL_WORKLOADS + SPLIT_WORKLOADS + FP8_WORKLOADS + F16_WORKLOADS:
         if w.name == name:
             return w
     raise KeyError(name)
@@ -158,6 +161,8 @@ def head_tensor(w: Workload, b: int, h: int, t: int) -> np.ndarray:
         x *= np.float32(PEAK_FACTOR)
     if w.dtype == "bf16":
         x = bf16_round(x)
+    elif w.dtype == "f16":
+        x = x.astype(np.float16).astype(np.float32)  # round to nearest even
     return x
 
 
@@ -169,9 +174,9 @@ def head_qkv(w: Workload, b: int, h: int):
 def _fill_one(args):
     w, b, h, t, path, offset = args
     x = head_tensor(w, b, h, t)
-    if w.dtype == "bf16":
+    if w.dtype in ("bf16", "f16"):
         arr = np.memmap(path, dtype=np.uint16, mode="r+", offset=offset, shape=(w.rows(t), w.D))
-        arr[:] = bf16_bits(x)
+        arr[:] = bf16_bits(x) if w.dtype == "bf16" else x.astype(np.float16).view(np.uint16)
     else:
         arr = np.memmap(path, dtype=np.float32, mode="r+", offset=offset, shape=(w.rows(t), w.D))
         arr[:] = x
@@ -185,7 +190,7 @@ def full_tensor(w: Workload, t: int, workers: int | None = None) -> np.ndarray:
 
     Slices are drawn in parallel worker processes when the tensor is large.
     """
-    dt = np.uint16 if w.dtype == "bf16" else np.float32
+    dt = np.uint16 if w.dtype in ("bf16", "f16") else np.float32
     shape = (w.B, w.H, w.rows(t), w.D)
     n_slices = w.B * w.H
     slice_elems = w.rows(t) * w.D
@@ -196,7 +201,8 @@ def full_tensor(w: Workload, t: int, workers: int | None = None) -> np.ndarray:
         for b in range(w.B):
             for h in range(w.H):
                 x = head_tensor(w, b, h, t)
-                out[b, h] = bf16_bits(x) if w.dtype == "bf16" else x
+                out[b, h] = bf16_bits(x) if w.dtype == "bf16" else \
+                    x.astype(np.float16).view(np.uint16) if w.dtype == "f16" else x
         return out
     import tempfile
     with tempfile.NamedTemporaryFile(dir="/dev/shm" if os.path.isdir("/dev/shm") else None,

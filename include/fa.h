@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 /* Identical to hipStream_t.  NULL means the device's null stream. */
 typedef struct ihipStream_t* fa_stream_t;
@@ -50,7 +50,8 @@ typedef struct ihipStream_t* fa_stream_t;
 /* Element type of q, k, v and o.  lse is always float32. */
 typedef enum fa_dtype {
   FA_DTYPE_F32 = 0,  /* IEEE binary32 in and out; float32 MFMA                     */
-  FA_DTYPE_BF16 = 1  /* bfloat16 in and out; products exact, sums and softmax fp32 */
+  FA_DTYPE_BF16 = 1, /* bfloat16 in and out; products exact, sums and softmax fp32 */
+  FA_DTYPE_F16 = 2   /* IEEE binary16 in and out; as bfloat16, P rounded to fp16   */
 } fa_dtype;
 
 typedef enum fa_status {
@@ -139,7 +140,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * most 64; so one range unless the queries are few against many keys.  *out and *splits_out are written only on FA_OK.
  * Returns FA_OK, FA_ERR_BAD_SHAPE (a size <= 0, Nq > Nk with
  * causal, n_splits outside 0..FA_SPLIT_MAX, overflow), FA_ERR_BAD_DTYPE,
- * FA_ERR_NULL_POINTER (out NULL) or FA_ERR_UNSUPPORTED (not bf16, D not in
+ * FA_ERR_NULL_POINTER (out NULL) or FA_ERR_UNSUPPORTED (float32, D not in
  * {64, 128}, Nq*D or Nk*D >= 2^31, more than 2^31-1 workgroups).
  */
 fa_status fa_fwd_split_query(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
@@ -158,8 +159,8 @@ fa_status fa_fwd_split_query(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
  * applied to whole ranges.  The pages name this use ("Flash-Decoding", same
  * page, section "Ergebnisse") without giving its steps.
  *
- * q, o      : [B, H, Nq, D] bfloat16 contiguous (o written).
- * k, v      : [B, H, Nk, D] bfloat16 contiguous; q, k, v may alias.
+ * q, o      : [B, H, Nq, D] bfloat16 or float16 contiguous (o written).
+ * k, v      : [B, H, Nk, D] of the same type, contiguous; q, k, v may alias.
  * lse       : float32 [B, H, Nq], written.
  * workspace : device scratch of workspace_bytes >= the size fa_fwd_split_query
  *             reports (may be NULL when that is 0), 16-byte aligned, not
@@ -171,7 +172,7 @@ fa_status fa_fwd_split_query(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
  *             is used and a single kernel writes o and lse.
  *
  * Validation and asynchrony as in fa_fwd; FA_ERR_WORKSPACE when workspace_bytes
- * is too small.  bfloat16 only.  Allocates nothing.
+ * is too small.  bfloat16 or float16 (not float32).  Allocates nothing.
  */
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,

@@ -27,8 +27,10 @@ from oracle import attention_ref
 TOL = {
     "f32": dict(o_max=1e-5, o_mean=None, lse=1e-3),
     "bf16": dict(o_max=2e-2, o_mean=2e-3, lse=1e-3),
+    # fp16 rounds P and O with unit roundoff 2^-11, a quarter of bf16's 2^-9
+    "f16": dict(o_max=5e-3, o_mean=5e-4, lse=1e-3),
 }
-TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def log(msg: str):
@@ -47,6 +49,8 @@ def to_device_bits(arr: np.ndarray, dtype: str) -> torch.Tensor:
     """Raw element bits (uint16 for bf16, float32) -> device tensor of that dtype."""
     if dtype == "bf16":
         t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.float16))
     else:
         t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
     return t.cuda()
@@ -56,6 +60,8 @@ def to_device_values(x: np.ndarray, dtype: str) -> torch.Tensor:
     """float32 values exactly representable in dtype -> device tensor of that dtype."""
     if dtype == "bf16":
         return to_device_bits(fi.bf16_bits(np.asarray(x, dtype=np.float32)), dtype)
+    if dtype == "f16":
+        return to_device_bits(np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16), dtype)
     return to_device_bits(np.asarray(x, dtype=np.float32), dtype)
 
 

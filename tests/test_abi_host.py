@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert fa.fa_abi_version() == 4
+    assert fa.fa_abi_version() == 5
     for st in range(10):
         s = fa.fa_status_str(st)
         assert s.startswith("FA_")
@@ -61,12 +61,17 @@ def test_query_sizes():
     assert st == fa.FA_OK and sz.workspace_bytes == 0
     st, sz = fa.fa_fwd_query(1, 1, 256, 64, 0, fa.FA_DTYPE_F32)
     assert st == fa.FA_OK and sz.q_bytes == 256 * 64 * 4
+    st, sz = fa.fa_fwd_query(1, 1, 256, 64, 0, fa.FA_DTYPE_F16)
+    assert st == fa.FA_OK and sz.q_bytes == 256 * 64 * 2
+    assert fa.fa_fwd_split_query(1, 1, 16, 256, 64, 1, 0, fa.FA_DTYPE_F16)[0] == fa.FA_OK
+    assert fa.fa_bwd_query(1, 1, 256, 64, 0, fa.FA_DTYPE_F16)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_query(1, 1, 1 << 24, 128, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_query(0, 1, 256, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
     assert fa.fa_fwd_query(1, 1, -3, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
     assert fa.fa_fwd_query(1 << 40, 1 << 40, 256, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
     assert fa.fa_fwd_query(1, 1, 256, 64, 0, 7)[0] == fa.FA_ERR_BAD_DTYPE
+    assert fa.fa_fwd_query(1, 1, 256, 64, 0, 3)[0] == fa.FA_ERR_BAD_DTYPE
     assert fa.lib().fa_fwd_query(1, 1, 256, 64, 0, 1, None) == fa.FA_ERR_NULL_POINTER
     # too many workgroups for one launch
     assert fa.fa_fwd_query(1 << 20, 1 << 10, 256, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
@@ -121,7 +126,7 @@ def test_valid_call_without_device_reports_hip_error():
 
 def test_binding_rejects_bad_tensors():
     import torch
-    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float64)
     with pytest.raises(TypeError):
         fa.attention_forward(q, q, q)
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
@@ -144,8 +149,9 @@ def test_every_kernel_stub_is_defined():
     undefined = [l for l in out.splitlines() if " U " in l and "_ZN2fa" in l]
     assert undefined == []
     kernels = set(re.findall(r"(_ZN2fa\d+fa_\w+_kernelI\w+)", out))
-    # bf16: D x causal x split; fp32: D x causal; merge: D; backward: 2 kernels x D x causal; fp8: D x causal
-    assert len(kernels) == 8 + 4 + 2 + 8 + 4, kernels
+    # bf16 and fp16: D x causal x split; fp32: D x causal; merge: D (bf16, fp16);
+    # backward: 2 kernels x D x causal; fp8: D x causal
+    assert len(kernels) == 16 + 4 + 4 + 8 + 4, kernels
 
 
 # ---------------------------------------------------------------- fa_fwd_split
