@@ -157,7 +157,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    names = [w.name for w in fi.ALL_WORKLOADS + fi.SPLIT_WORKLOADS + fi.FP8_WORKLOADS + fi.F16_WORKLOADS] \
+    names = [w.name for w in fi.ALL_WORKLOADS + fi.SPLIT_WORKLOADS + fi.FP8_WORKLOADS + fi.BREADTH_WORKLOADS] \
         if args.sweep \
         else [args.workload]
     for name in names:

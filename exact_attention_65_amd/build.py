@@ -22,8 +22,12 @@ SOURCES = [os.path.join(CSRC, "fa_check.cpp"), os.path.join(CSRC, "fa_fwd.hip"),
            os.path.join(CSRC, "fa_fp8.hip")]
 ARCH = "gfx950"
 
-# Packed fp32 VALU instructions are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU instructions are disabled for all device code.  The kernels'
+# slot loops must unroll completely (their fragment arrays then live in
+# registers); at head dimension 256 they exceed the default size limit of an
+# unroll requested by pragma, and the arrays fall back to scratch memory.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-pragma-unroll-threshold=1000000"]
 COMMON = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC] + DEVICE_FLAGS
 
 

@@ -39,8 +39,8 @@ fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, fa_
   return FA_OK;
 }
 
-fa_status check_supported(int64_t B, int64_t H, int64_t N, int64_t D) {
-  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+fa_status check_supported(int64_t B, int64_t H, int64_t N, int64_t D, bool wide) {
+  if (D != 64 && D != 128 && !(wide && (D == 96 || D == 256))) return FA_ERR_UNSUPPORTED;
   // offsets inside one (b, h) slice are 32-bit
   if (N * D > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
   const int64_t qblocks = (N + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -70,7 +70,7 @@ fa_status check_call(const void* q, const void* k, const void* v, const void* o,
   for (const void* p : ins)
     if (overlaps(o, sz.o_bytes, p, sz.q_bytes) || overlaps(lse, sz.lse_bytes, p, sz.q_bytes))
       return FA_ERR_ALIASING;
-  return check_supported(B, H, N, D);
+  return check_supported(B, H, N, D, dtype != FA_DTYPE_F32);
 }
 
 // Number of key ranges: the requested count, or for FA_SPLIT_AUTO enough for
@@ -105,7 +105,7 @@ fa_status check_split_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_
     return FA_ERR_BAD_SHAPE;
   if (qbytes > (uint64_t)SIZE_MAX || kbytes > (uint64_t)SIZE_MAX) return FA_ERR_BAD_SHAPE;
   // the arguments are valid; what follows decides whether the kernels support them
-  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 96 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
   if (dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
   if (Nq * D > (int64_t)INT32_MAX || Nk * D > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
   const int64_t qblocks = (Nq + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -259,7 +259,7 @@ __attribute__((visibility("default"))) fa_status fa_fwd_query(int64_t B, int64_t
   if (!out) return FA_ERR_NULL_POINTER;
   fa_status st = fa::check_shape(B, H, N, D, (int)dtype, out);
   if (st != FA_OK) return st;
-  return fa::check_supported(B, H, N, D);
+  return fa::check_supported(B, H, N, D, dtype != FA_DTYPE_F32);
 }
 
 __attribute__((visibility("default"))) const char* fa_status_str(fa_status s) {

@@ -17,8 +17,9 @@ size_t elem_size(int dtype);
 // Shape/dtype validation shared by both entry points; fills sizes on success.
 fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, fa_sizes* sizes);
 
-// Whether a valid shape is one the kernels are built for.
-fa_status check_supported(int64_t B, int64_t H, int64_t N, int64_t D);
+// Whether a valid shape is one the kernels are built for.  D = 96 and 256
+// exist only for the 16-bit forward kernels (wide = true).
+fa_status check_supported(int64_t B, int64_t H, int64_t N, int64_t D, bool wide = false);
 
 // Full validation of an fa_fwd call, without touching the device.
 fa_status check_call(const void* q, const void* k, const void* v, const void* o, const void* lse,

@@ -54,11 +54,19 @@ template <bool SPLIT>
 hipError_t launch_h16(int dtype, int D, bool causal, const FwdArgs& a, hipStream_t s) {
   const int t = kBF16Threads, n = a.n_blocks;
   if (dtype == FA_DTYPE_F16) {
+    if (D == 256) return causal ? launch(fa_fwd_f16_kernel<256, true, SPLIT>, n, a, t, s)
+                                : launch(fa_fwd_f16_kernel<256, false, SPLIT>, n, a, t, s);
+    if (D == 96) return causal ? launch(fa_fwd_f16_kernel<96, true, SPLIT>, n, a, t, s)
+                               : launch(fa_fwd_f16_kernel<96, false, SPLIT>, n, a, t, s);
     if (D == 128) return causal ? launch(fa_fwd_f16_kernel<128, true, SPLIT>, n, a, t, s)
                                 : launch(fa_fwd_f16_kernel<128, false, SPLIT>, n, a, t, s);
     return causal ? launch(fa_fwd_f16_kernel<64, true, SPLIT>, n, a, t, s)
                   : launch(fa_fwd_f16_kernel<64, false, SPLIT>, n, a, t, s);
   }
+  if (D == 256) return causal ? launch(fa_fwd_bf16_kernel<256, true, SPLIT>, n, a, t, s)
+                              : launch(fa_fwd_bf16_kernel<256, false, SPLIT>, n, a, t, s);
+  if (D == 96) return causal ? launch(fa_fwd_bf16_kernel<96, true, SPLIT>, n, a, t, s)
+                             : launch(fa_fwd_bf16_kernel<96, false, SPLIT>, n, a, t, s);
   if (D == 128) return causal ? launch(fa_fwd_bf16_kernel<128, true, SPLIT>, n, a, t, s)
                               : launch(fa_fwd_bf16_kernel<128, false, SPLIT>, n, a, t, s);
   return causal ? launch(fa_fwd_bf16_kernel<64, true, SPLIT>, n, a, t, s)
@@ -80,8 +88,12 @@ hipError_t launch_combine(int dtype, int D, const FwdArgs& a, hipStream_t s) {
   const int per_block = kCombineThreads / (D / 8);
   const int blocks = (int)((rows + per_block - 1) / per_block);
   if (dtype == FA_DTYPE_F16)
-    return D == 128 ? launch(fa_combine_f16_kernel<128>, blocks, a, kCombineThreads, s)
-                    : launch(fa_combine_f16_kernel<64>, blocks, a, kCombineThreads, s);
+    return D == 256   ? launch(fa_combine_f16_kernel<256>, blocks, a, kCombineThreads, s)
+           : D == 128 ? launch(fa_combine_f16_kernel<128>, blocks, a, kCombineThreads, s)
+           : D == 96  ? launch(fa_combine_f16_kernel<96>, blocks, a, kCombineThreads, s)
+                      : launch(fa_combine_f16_kernel<64>, blocks, a, kCombineThreads, s);
+  if (D == 256) return launch(fa_combine_kernel<256>, blocks, a, kCombineThreads, s);
+  if (D == 96) return launch(fa_combine_kernel<96>, blocks, a, kCombineThreads, s);
   if (D == 128) return launch(fa_combine_kernel<128>, blocks, a, kCombineThreads, s);
   return launch(fa_combine_kernel<64>, blocks, a, kCombineThreads, s);
 }

@@ -212,13 +212,13 @@ __device__ __forceinline__ void online_softmax(float (&s)[NS], float c, float& m
 // (ds_read_b64_tr_b16), which on this pattern runs near the plain read's rate.
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
-  if constexpr (D == 128) return swap23(row & 15);
+  if constexpr (D >= 128) return swap23(row & 15);
   else return ((row ^ (row >> 2)) & 1) | (row & 2) | ((row >> 1) & 4);
 }
 template <int D>
 __device__ __forceinline__ int vswz(int key) {
   const int r = key & 3;
-  if constexpr (D == 128) return 4 * r | (r & 2);
+  if constexpr (D >= 128) return 4 * r | (r & 2);
   else return 2 * r;
 }
 
@@ -268,21 +268,31 @@ template <typename E, int D, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   typedef typename E::vec8 vec8;
   constexpr int BN = 64;                // keys per tile
-  constexpr int RB = D * 2;             // bytes per K / V row
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  // D = 96 rows are stored in LDS as 128-wide rows whose last 4 chunks stay
+  // zero (so are Q's columns 96 .. 127): every LDS address and MFMA step is
+  // the D = 128 one; global rows keep their real width
+  constexpr int DP = D == 96 ? 128 : D; // head dimension of the LDS layout and the MFMAs
+  constexpr int GRB = D * 2;            // bytes per global K / V row
+  constexpr int RB = DP * 2;            // bytes per LDS K / V row
+  constexpr int CPR = DP / 8;           // 16-byte chunks per LDS row
   constexpr int RPB = 64 / CPR;         // rows per 1 KB block (one wave-wide load)
   constexpr int TILE16 = BN * CPR;      // 16-byte chunks per tile
   constexpr int NLD = TILE16 / 64 / 4;  // 1 KB K loads per wave per tile
   constexpr int NKB = BN / 32;          // 32-key MFMA blocks per tile
-  constexpr int NDB = D / 32;           // 32-wide d blocks of O
-  constexpr int NKK = D / 16;           // 16-deep steps of the score contraction
+  constexpr int NDB = DP / 32;          // 32-wide d blocks of O
+  constexpr int NKK = DP / 16;          // 16-deep steps of the score contraction
   constexpr int NCC = BN / 16;          // 16-key steps of the value contraction
   constexpr int NSA = NKK * NKB;        // score MFMAs per tile (phase A slots)
   constexpr int NSB = NDB * NCC;        // value MFMAs per tile (phase B slots)
   constexpr int PFA = 3;                // score-fragment reads in flight in phase A
   constexpr int PFB = 4;                // value-fragment reads in flight in phase B
   static_assert(NLD >= 1, "tile loads");
-  static_assert(NSA == 16 && NSB == 16 || D == 64, "slot counts");
+  static_assert(NSA == 2 * DP / 16 && NSB == DP / 8, "slot counts");
+  // fragment arrays: one entry per slot, or at D = 256 (32 slots a phase) a
+  // ring of PF + 1 entries, which the compiler keeps in registers where it
+  // puts a 32-entry array in scratch memory
+  constexpr int RKA = D == 256 ? PFA + 1 : NSA;
+  constexpr int RVB = D == 256 ? PFB + 1 : NSB;
 
   // four separate arrays, picked at compile time by the two-step unrolled loop:
   // the compiler then sees that a tile load into one buffer cannot alias reads
@@ -344,26 +354,36 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < NQ) x = *(const u32x4*)(Qg + (size_t)qrow * D + 16 * kk + 8 * h) ^ flip;
+      const bool col_ok = D == DP || 16 * kk + 8 * h < D;  // columns past D stay zero
+      if (qrow < NQ && col_ok) x = *(const u32x4*)(Qg + (size_t)qrow * D + 16 * kk + 8 * h) ^ flip;
       qf[kk] = __builtin_bit_cast(vec8, x);
     }
   }
 
   // tile DMA: per-lane byte offsets (fixed for every tile)
+  // (LDS position cl of a row holds global chunk cl ^ swizzle(row); at D = 96
+  // the lanes whose chunk is past the row load nothing)
   uint32_t koff[NLD], voff[NLD];
+  bool kon[NLD], von[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int row = (wave * NLD + i) * RPB + lane / CPR;
     const int cl = lane % CPR;
-    koff[i] = row * RB + ((cl ^ kswz<D>(row)) * 16);
-    voff[i] = row * RB + ((cl ^ vswz<D>(row)) * 16);
+    const int kg = cl ^ kswz<DP>(row), vg = cl ^ vswz<DP>(row);
+    koff[i] = row * GRB + kg * 16;
+    voff[i] = row * GRB + vg * 16;
+    kon[i] = kg < D / 8;
+    von[i] = vg < D / 8;
   }
-  auto issue = [&](u32x4* dst, const uint16_t* src, const uint32_t (&off)[NLD], int kv0)
+  auto issue = [&](u32x4* dst, const uint16_t* src, const uint32_t (&off)[NLD], const bool (&on)[NLD], int kv0)
       __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(NK - kv0) * RB), kRsrcWord3);
+        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(NK - kv0) * GRB), kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) lds_load16(r, dst + (wave * NLD + i) * 64, off[i]);
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (D == DP) lds_load16(r, dst + (wave * NLD + i) * 64, off[i]);
+      else if (on[i]) lds_load16(r, dst + (wave * NLD + i) * 64, off[i]);
+    }
   };
 
   // per-lane LDS read addresses (bytes).  K operand of score slot (kk, kb): row
@@ -374,13 +394,13 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   // XOR (db << 6), key step cc adds 16 rows.
   const uint32_t kaddr0 = [&] {
     const int row = swap23(c32);
-    return (uint32_t)(row * RB + ((h ^ kswz<D>(row)) * 16));
+    return (uint32_t)(row * RB + ((h ^ kswz<DP>(row)) * 16));
   }();
   const uint32_t vaddr0 = [&] {
     const int g = lane >> 4, i16 = lane & 15;
     const int hh = g >> 1, gg = g & 1, r = i16 >> 2, q = i16 & 3;
     const int chunk = 2 * gg + (q >> 1);
-    return (uint32_t)((8 * hh + r) * RB + ((chunk ^ vswz<D>(r)) * 16) + (q & 1) * 8);
+    return (uint32_t)((8 * hh + r) * RB + ((chunk ^ vswz<DP>(r)) * 16) + (q & 1) * 8);
   }();
   auto kfrag = [&](const u32x4* Kt, int s) __attribute__((always_inline)) {
     const int kk = s / NKB, kb = s % NKB;
@@ -492,25 +512,25 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   // reads of phase B's first value fragments (from Vc) so that phase B does
   // not begin by waiting on LDS.
   auto phase_a = [&](f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], const u32x4* Kt, const u32x4* Vc,
-                     u32x4 (&vf)[NSB]) __attribute__((always_inline)) {
+                     u32x4 (&vf)[RVB]) __attribute__((always_inline)) {
     constexpr int NP = 2 * NCC;  // p slices (4 scores each)
     constexpr int SLOTS = NSA > NP ? NSA : NP;
     static_assert(PFB <= SLOTS && PFA <= NSA, "prefetch depths");
     lsum[0] = lsum[1] = xsum[0] = xsum[1] = 0.0f;
-    u32x4 kf[NSA];
+    u32x4 kf[RKA];
 #pragma unroll
-    for (int k = 0; k < PFA; ++k) kf[k] = kfrag(Kt, k);
+    for (int k = 0; k < PFA; ++k) kf[k % RKA] = kfrag(Kt, k);
     u32x2 pw[NP];
 #pragma unroll
     for (int k = 0; k < SLOTS; ++k) {
-      if (k + PFA < NSA) kf[k + PFA] = kfrag(Kt, k + PFA);
-      if (k >= SLOTS - PFB) vf[k - (SLOTS - PFB)] = vfrag(Vc, k - (SLOTS - PFB));
+      if (k + PFA < NSA) kf[(k + PFA) % RKA] = kfrag(Kt, k + PFA);
+      if (k >= SLOTS - PFB) vf[(k - (SLOTS - PFB)) % RVB] = vfrag(Vc, k - (SLOTS - PFB));
 #pragma unroll
       for (int q = k * NP / SLOTS; q < (k + 1) * NP / SLOTS; ++q) pw[q] = p_slice(sc, q >> 1, q & 1);
       if (k < NSA) {
         const int kk = k / NKB, kb = k % NKB;
         const f32x16 z = {};
-        sn[kb] = E::mfma(__builtin_bit_cast(vec8, kf[k]), qf[kk], kk == 0 ? z : sn[kb]);
+        sn[kb] = E::mfma(__builtin_bit_cast(vec8, kf[k % RKA]), qf[kk], kk == 0 ? z : sn[kb]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -525,15 +545,15 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   // phase B of iteration j: value MFMAs of tile j (V^T from Vt, P^T in pf;
   // fragments 0 .. PFB-1 already requested in phase A) beside the reference
   // update of tile j+1's scores in sn
-  auto phase_b = [&](const f32x16 (&sn)[NKB], const u32x4* Vt, u32x4 (&vf)[NSB]) __attribute__((always_inline)) {
+  auto phase_b = [&](const f32x16 (&sn)[NKB], const u32x4* Vt, u32x4 (&vf)[RVB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
-      if (k + PFB < NSB) vf[k + PFB] = vfrag(Vt, k + PFB);
+      if (k + PFB < NSB) vf[(k + PFB) % RVB] = vfrag(Vt, k + PFB);
       // the reference slices go in the early slots so the update is known
       // well before the next phase needs mu
       if (k <= NKB) ref_slice(sn, k);
       const int db = k % NDB, cc = k / NDB;
-      o[db] = E::mfma(__builtin_bit_cast(vec8, vf[k]), pf[cc], o[db]);
+      o[db] = E::mfma(__builtin_bit_cast(vec8, vf[k % RVB]), pf[cc], o[db]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -550,10 +570,10 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   // ---- prologue ------------------------------------------------------------
   __syncthreads();  // zeroed K tiles visible before any load lands
   if (n_loc > 0) {
-    issue(kA, Kg, koff, t_lo * BN);
-    issue(vA, Vg, voff, t_lo * BN);
+    issue(kA, Kg, koff, kon, t_lo * BN);
+    issue(vA, Vg, voff, von, t_lo * BN);
   }
-  if (n_loc > 1) issue(kB, Kg, koff, (t_lo + 1) * BN);
+  if (n_loc > 1) issue(kB, Kg, koff, kon, (t_lo + 1) * BN);
   __syncthreads();  // the first two K tiles and the first V tile in LDS
   if (n_vis > 0) {
     // scores of the first tile and their reference (the running sums are still zero)
@@ -581,15 +601,15 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
     // (it keeps it only at the barrier inside the loop body).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < n_loc) issue(Vd, Vg, voff, (t_lo + j + 1) * BN);
-    if (j + 2 < n_loc) issue(Kd, Kg, koff, (t_lo + j + 2) * BN);
+    if (j + 1 < n_loc) issue(Vd, Vg, voff, von, (t_lo + j + 1) * BN);
+    if (j + 2 < n_loc) issue(Kd, Kg, koff, kon, (t_lo + j + 2) * BN);
     if (j >= n_vis) return;  // nothing of this tile or later is visible to this wave
     // One code path for every iteration (a second one for the last tile costs
     // more registers than the chip has): after the last visible tile the
     // "next" scores are computed from whatever K buffer is there and then fully
     // masked (they lie past the key range or after every query of the wave),
     // which leaves the reference and the sums unchanged, and are never used.
-    u32x4 vf[NSB];
+    u32x4 vf[RVB];
     phase_a(sc, sn, Kn, Vc, vf);
     apply_rescale();
     mask(sn, t_lo + j + 1);
@@ -615,6 +635,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = 32 * db + 8 * g + 4 * h;
+          if (32 * db >= D) continue;
           const f32x4 w = {o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
                            o[db][4 * g + 3] * inv};
           *(f32x4*)(Op + d) = w;
@@ -627,6 +648,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = 32 * db + 8 * g + 4 * h;
+          if (32 * db >= D) continue;
           const u32x2 w = {E::pack(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
                            E::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
           *(u32x2*)(Og + d) = w;
@@ -636,12 +658,14 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   }
 }
 
+// D = 256 holds 64 Q and 128 output registers per lane and 128 KB of tiles:
+// one workgroup per CU, one wave per SIMD.
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kBF16Threads, D == 256 ? 1 : 2) void fa_fwd_bf16_kernel(FwdArgs a) {
   fwd16_body<BF16, D, CAUSAL, SPLIT>(a);
 }
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(kBF16Threads, 2) void fa_fwd_f16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kBF16Threads, D == 256 ? 1 : 2) void fa_fwd_f16_kernel(FwdArgs a) {
   fwd16_body<F16, D, CAUSAL, SPLIT>(a);
 }
 
@@ -661,6 +685,7 @@ __device__ __forceinline__ void combine_body(const FwdArgs& a) {
   constexpr int TPR = D / 8;                       // lanes per row
   constexpr int RPB = kCombineThreads / TPR;       // rows per workgroup
   const int tid = threadIdx.x;
+  if (tid >= RPB * TPR) return;  // D = 96: 12 lanes a row leave 4 of 256 idle
   const long long row = (long long)blockIdx.x * RPB + tid / TPR;
   const int d0 = (tid % TPR) * 8;
   if (row >= (long long)a.n_bh * a.nq) return;

@@ -111,11 +111,14 @@ FP8_N4096 = Workload("fp8_b2_h32_n4096_d128", 6, 2, 32, 4096, 128, "fp8", False)
 FP8_WORKLOADS = (FP8_N4096,)
 # fp16 inputs at the headline shape
 F16_N4096 = Workload("f16_b2_h32_n4096_d128", 7, 2, 32, 4096, 128, "f16", False)
-F16_WORKLOADS = (F16_N4096,)
+# head dimension 256: the headline's bytes with half the heads; head dimension 96
+D256_N4096 = Workload("bf16_b2_h16_n4096_d256", 8, 2, 16, 4096, 256, "bf16", False)
+D96_N4096 = Workload("bf16_b2_h32_n4096_d96", 9, 2, 32, 4096, 96, "bf16", False)
+BREADTH_WORKLOADS = (F16_N4096, D256_N4096, D96_N4096)
 
 
 def workload_by_name(name: str) -> Workload:
-    for w in ALL_WORKLOADS + SPLIT_WORKLOADS + FP8_WORKLOADS + F16_WORKLOADS:
+    for w in ALL_WORKLOADS + SPLIT_WORKLOADS + FP8_WORKLOADS + BREADTH_WORKLOADS:
         if w.name == name:
             return w
     raise KeyError(name)

@@ -65,7 +65,15 @@ def test_query_sizes():
     assert st == fa.FA_OK and sz.q_bytes == 256 * 64 * 2
     assert fa.fa_fwd_split_query(1, 1, 16, 256, 64, 1, 0, fa.FA_DTYPE_F16)[0] == fa.FA_OK
     assert fa.fa_bwd_query(1, 1, 256, 64, 0, fa.FA_DTYPE_F16)[0] == fa.FA_ERR_UNSUPPORTED
-    assert fa.fa_fwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
+    assert fa.fa_fwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_F32)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_query(1, 1, 256, 80, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_query(1, 1, 256, 256, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
+    assert fa.fa_fwd_query(1, 1, 256, 256, 0, fa.FA_DTYPE_F16)[0] == fa.FA_OK
+    assert fa.fa_fwd_query(1, 1, 256, 256, 0, fa.FA_DTYPE_F32)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_split_query(1, 1, 16, 512, 256, 1, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
+    assert fa.fa_bwd_query(1, 1, 256, 256, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_fp8_query(1, 1, 256, 256, 0)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_query(1, 1, 1 << 24, 128, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_query(0, 1, 256, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
     assert fa.fa_fwd_query(1, 1, -3, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
@@ -102,7 +110,7 @@ def call(q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, lse=A + 4 * SZ, B=1, H=2, N=
     (dict(o=A + 2 * SZ + 2 * 100 * 64 * 2 - 16), fa.FA_ERR_ALIASING),  # o starts in v's last 16 bytes
     (dict(o=A + 2 * SZ + 2 * 100 * 64 * 2), fa.FA_ERR_HIP),  # o right after v: valid
     (dict(lse=A), fa.FA_ERR_ALIASING),                  # lse on top of q
-    (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=80), fa.FA_ERR_UNSUPPORTED),
     (dict(D=32), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_validation_before_any_device_call(kw, expect):
@@ -149,9 +157,9 @@ def test_every_kernel_stub_is_defined():
     undefined = [l for l in out.splitlines() if " U " in l and "_ZN2fa" in l]
     assert undefined == []
     kernels = set(re.findall(r"(_ZN2fa\d+fa_\w+_kernelI\w+)", out))
-    # bf16 and fp16: D x causal x split; fp32: D x causal; merge: D (bf16, fp16);
+    # bf16 and fp16: D (64, 96, 128, 256) x causal x split; fp32: D x causal; merge: D x (bf16, fp16);
     # backward: 2 kernels x D x causal; fp8: D x causal
-    assert len(kernels) == 16 + 4 + 4 + 8 + 4, kernels
+    assert len(kernels) == 32 + 4 + 8 + 8 + 4, kernels
 
 
 # ---------------------------------------------------------------- fa_fwd_split
@@ -193,7 +201,8 @@ def test_split_query_sizes_and_ranges():
     ((1, 1, 4, 64, 64, 0, 257, fa.FA_DTYPE_BF16), fa.FA_ERR_BAD_SHAPE),
     ((1, 1, 4, 64, 64, 0, 256, fa.FA_DTYPE_BF16), fa.FA_OK),
     ((1, 1, 4, 64, 64, 0, 0, fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
-    ((1, 1, 4, 64, 96, 0, 0, fa.FA_DTYPE_BF16), fa.FA_ERR_UNSUPPORTED),
+    ((1, 1, 4, 64, 80, 0, 0, fa.FA_DTYPE_BF16), fa.FA_ERR_UNSUPPORTED),
+    ((1, 1, 4, 64, 96, 0, 0, fa.FA_DTYPE_BF16), fa.FA_OK),
     ((1, 1, 4, 64, 64, 0, 0, 3), fa.FA_ERR_BAD_DTYPE),
 ])
 def test_split_query_validation(args, expect):

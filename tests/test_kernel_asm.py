@@ -57,14 +57,14 @@ def _barrier_waits(body: str):
 
 def test_bf16_kernels_present(asm):
     names = [n for n, _ in _kernels(asm)]
-    assert sum("fwd_bf16" in n for n in names) == 8, names
-    assert sum("fwd_f16" in n for n in names) == 8, names
-    assert sum("combine" in n for n in names) == 4, names
+    assert sum("fwd_bf16" in n for n in names) == 16, names
+    assert sum("fwd_f16" in n for n in names) == 16, names
+    assert sum("combine" in n for n in names) == 8, names
 
 
 def test_every_tile_barrier_drains_vmcnt(asm):
     kernels = [(n, b) for n, b in _kernels(asm) if "fwd_bf16" in n or "fwd_f16" in n]
-    assert len(kernels) == 16
+    assert len(kernels) == 32
     for name, body in kernels:
         waits = _barrier_waits(body)
         assert waits, f"{name}: no barrier after a tile load"
@@ -106,3 +106,13 @@ def test_fp8_kernels_barriers_drain_vmcnt_and_do_not_spill(fp8_asm):
         assert not bad, f"{name}: barrier(s) at asm line(s) {bad} do not wait for the LDS tile loads"
     for m in re.finditer(r"\.name:\s+(_ZN2fa\w*fp8\w*)\s.*?\.vgpr_spill_count:\s+(\d+)", fp8_asm, re.S):
         assert int(m.group(2)) == 0, m.group(1)
+
+
+@pytest.mark.parametrize("source", ["fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip"])
+def test_no_kernel_uses_scratch_memory(source):
+    """Register arrays that the compiler cannot keep in registers go to scratch
+    memory, silently and at a large cost (it happened at head dimension 256)."""
+    text = fabuild.device_asm(source)
+    sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)\n(?:.*\n){0,40}?\s+\.name:\s+(\S+)", text)
+    assert sizes, "no kernel metadata found"
+    assert all(int(n) == 0 for n, _ in sizes), [(k, n) for n, k in sizes if int(n)]
