@@ -146,7 +146,7 @@ def test_non_default_stream():
 
 def test_status_errors_on_device():
     import exact_attention_65_amd as fa
-    q = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(1, 1, 64, 80, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fa.FaError) as e:
         fa.attention_forward(q, q, q)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
