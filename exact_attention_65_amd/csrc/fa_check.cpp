@@ -79,8 +79,17 @@ fa_status check_call(const void* q, const void* k, const void* v, const void* o,
 // range, keeps the partial results (Nq rows of D+1 floats per range) within a
 // quarter of the K/V bytes (S <= Nk / (4 Nq)), and at most 64.  Square shapes
 // therefore stay on one range: their partial results would double the traffic.
-static int resolve_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int requested) {
+// For one query row (the vector-unit kernel): enough ranges for about 512
+// workgroups (two waves per SIMD; measured, more ranges only add merge work),
+// each range at least 1024 keys, at most 64.
+static int resolve_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int requested) {
   if (requested != FA_SPLIT_AUTO) return requested;
+  if (uses_decode_kernel(Nq, D)) {
+    int64_t s = (512 + B * H - 1) / (B * H);
+    if (s > Nk / 1024) s = Nk / 1024;
+    if (s > 64) s = 64;
+    return s < 1 ? 1 : (int)s;
+  }
   const int64_t blocks = B * H * ((Nq + kRowsPerBlock - 1) / kRowsPerBlock);
   const int64_t tiles = (Nk + kKeysPerTile - 1) / kKeysPerTile;
   int64_t s = (512 + blocks - 1) / blocks;
@@ -110,7 +119,7 @@ fa_status check_split_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_
   if (Nq * D > (int64_t)INT32_MAX || Nk * D > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
   const int64_t qblocks = (Nq + kRowsPerBlock - 1) / kRowsPerBlock;
   if (B > kMaxGrid / H || B * H > kMaxGrid / qblocks) return FA_ERR_UNSUPPORTED;
-  const int s = resolve_splits(B, H, Nq, Nk, n_splits);
+  const int s = resolve_splits(B, H, Nq, Nk, D, n_splits);
   if (B * H * qblocks > kMaxGrid / s) return FA_ERR_UNSUPPORTED;
   uint64_t ws = 0;
   if (s > 1 && (!mul_ok(qrows, (uint64_t)(D + 1) * 4, &ws) || !mul_ok(ws, (uint64_t)s, &ws)))

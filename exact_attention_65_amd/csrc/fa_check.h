@@ -28,6 +28,9 @@ fa_status check_call(const void* q, const void* k, const void* v, const void* o,
 // Keys per tile of the bf16 kernel (the unit a key range is made of).
 constexpr int64_t kKeysPerTile = 64;
 
+// Whether fa_fwd_split runs the one-query-row kernel (Nq = 1, D in {64, 128, 256}).
+inline bool uses_decode_kernel(int64_t Nq, int64_t D) { return Nq == 1 && (D == 64 || D == 128 || D == 256); }
+
 // fa_fwd_split_query: sizes and the resolved number of key ranges.
 fa_status check_split_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
                             int n_splits, int dtype, fa_sizes* sizes, int* splits);

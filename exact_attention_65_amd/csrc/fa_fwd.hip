@@ -21,6 +21,7 @@
 #include "fa.h"
 #include "fa_check.h"
 #include "fa_device.h"
+#include "fa_decode_kernel.hpp"
 #include "fa_fwd_kernel.hpp"
 
 namespace fa {
@@ -98,6 +99,18 @@ hipError_t launch_combine(int dtype, int D, const FwdArgs& a, hipStream_t s) {
   return launch(fa_combine_kernel<64>, blocks, a, kCombineThreads, s);
 }
 
+// one query row per (b, h): the vector-unit key-range kernel
+hipError_t launch_decode(int dtype, int D, const FwdArgs& a, hipStream_t s) {
+  const int n = a.n_bh * a.n_split, t = kDecodeThreads;
+  if (dtype == FA_DTYPE_F16)
+    return D == 256   ? launch(fa_decode_kernel<F16, 256>, n, a, t, s)
+           : D == 128 ? launch(fa_decode_kernel<F16, 128>, n, a, t, s)
+                      : launch(fa_decode_kernel<F16, 64>, n, a, t, s);
+  return D == 256   ? launch(fa_decode_kernel<BF16, 256>, n, a, t, s)
+         : D == 128 ? launch(fa_decode_kernel<BF16, 128>, n, a, t, s)
+                    : launch(fa_decode_kernel<BF16, 64>, n, a, t, s);
+}
+
 // Arguments shared by both entry points.  scale: |scale| log2(e) for exp2, the
 // sign applied to Q's bits.
 FwdArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
@@ -162,6 +175,16 @@ extern "C" __attribute__((visibility("default"))) fa_status fa_fwd_split(
 
   fa::FwdArgs a = fa::make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, (int)dtype, fa::kBF16Rows, splits);
   const hipStream_t s = (hipStream_t)stream;
+  if (fa::uses_decode_kernel(Nq, D)) {
+    // one query row: every key is visible to it, with or without the causal mask
+    if (splits > 1) {
+      a.o_part = (float*)workspace;
+      a.lse_part = a.o_part + (size_t)splits * a.n_bh * a.nq * D;
+    }
+    if (fa::launch_decode((int)dtype, (int)D, a, s) != hipSuccess) return FA_ERR_HIP;
+    if (splits == 1) return FA_OK;
+    return fa::launch_combine((int)dtype, (int)D, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
   if (splits == 1)
     return fa::launch_h16<false>((int)dtype, (int)D, causal != 0, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
   // workspace: [splits][B*H][Nq][D] float outputs, then [splits][B*H][Nq] log-sum-exps

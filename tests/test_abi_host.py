@@ -158,8 +158,8 @@ def test_every_kernel_stub_is_defined():
     assert undefined == []
     kernels = set(re.findall(r"(_ZN2fa\d+fa_\w+_kernelI\w+)", out))
     # bf16 and fp16: D (64, 96, 128, 256) x causal x split; fp32: D x causal; merge: D x (bf16, fp16);
-    # backward: 2 kernels x D x causal; fp8: D x causal
-    assert len(kernels) == 32 + 4 + 8 + 8 + 4, kernels
+    # backward: 2 kernels x D x causal; fp8: D x causal; one-query-row: (bf16, fp16) x D (64, 128, 256)
+    assert len(kernels) == 32 + 4 + 8 + 8 + 4 + 6, kernels
 
 
 # ---------------------------------------------------------------- fa_fwd_split
@@ -169,8 +169,14 @@ def test_split_query_sizes_and_ranges():
     assert sz.q_bytes == sz.o_bytes == 4 * 32 * 1 * 128 * 2
     assert sz.k_bytes == sz.v_bytes == 4 * 32 * 16384 * 128 * 2
     assert sz.lse_bytes == 4 * 32 * 4
-    # 128 query blocks: 4 ranges give 512 workgroups
+    # one query row: the vector-unit kernel, 4 ranges give 512 workgroups
     assert s == 4 and sz.workspace_bytes == 4 * 4 * 32 * 1 * (128 + 1) * 4
+    # ... with at least 1024 keys a range
+    st, sz, s = fa.fa_fwd_split_query(1, 1, 1, 5000, 64, 0, fa.FA_SPLIT_AUTO, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK and s == 4
+    # ... but not at D = 96 (the 128-row kernel's rule: 8 tiles a range)
+    st, sz, s = fa.fa_fwd_split_query(1, 1, 1, 5000, 96, 0, fa.FA_SPLIT_AUTO, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK and s == 9
     # one range: no workspace
     st, sz, s = fa.fa_fwd_split_query(2, 32, 4096, 4096, 128, 0, 1, fa.FA_DTYPE_BF16)
     assert st == fa.FA_OK and s == 1 and sz.workspace_bytes == 0
