@@ -259,11 +259,11 @@ __global__ __launch_bounds__(kFp8Threads, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      for (int i = 0; i < 16; ++i) mx = vmax(mx, s[kb][i]);
     mx = pair_max(mx);
     const float mt = mx * c;
     if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0) {
-      const float m_new = fmaxf(m_ref, mt);
+      const float m_new = vmax(m_ref, mt);
       const float alpha = m_new == neg_inf() ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)

@@ -140,6 +140,12 @@ struct F16 {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Maximum that propagates NaN (IEEE maximum).  It lowers to v_maximum3_f32,
+// two new operands per instruction; fmaxf (maxNum) makes the compiler first
+// quieten every operand that is not known to be canonical, such as MFMA
+// results, with an extra v_max each.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Pins a value in place: the empty asm "reads and rewrites" it, so its
 // computation cannot be moved past this point (the optimiser otherwise sinks
 // arithmetic toward its first use, out of the slot it was placed in).
@@ -159,7 +165,7 @@ __device__ __forceinline__ void swap_halves(uint32_t& a, uint32_t& b) {
 __device__ __forceinline__ float pair_max(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   swap_halves(a, b);
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  return vmax(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
@@ -457,17 +463,17 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
     if (k < NKB) {
       float mx = s[k][0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[k][i]);
+      for (int i = 1; i < 16; ++i) mx = vmax(mx, s[k][i]);
       pin(mx);
       mpart[k] = mx;
     } else {
       float mx = mpart[0];
 #pragma unroll
-      for (int kb = 1; kb < NKB; ++kb) mx = fmaxf(mx, mpart[kb]);
+      for (int kb = 1; kb < NKB; ++kb) mx = vmax(mx, mpart[kb]);
       mx = pair_max(mx);
       const float mt = mx * c;
       const bool any = __builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0;
-      const float m_new = any ? fmaxf(m_ref, mt) : m_ref;
+      const float m_new = any ? vmax(m_ref, mt) : m_ref;
       const float alpha = m_new == neg_inf() ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
       l *= alpha;
       lx *= alpha;
@@ -494,8 +500,10 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
     const uint32_t w1 = E::pack(s[kb][base + 2], s[kb][base + 3]);
     lsum[half] = E::sum2(w0, lsum[half]);
     lsum[half] = E::sum2(w1, lsum[half]);
-    xsum[half] += s[kb][base + 0] + s[kb][base + 1];
-    xsum[half] += s[kb][base + 2] + s[kb][base + 3];
+    // the first slice of a phase starts the fp32 sum (adding it to a zero
+    // would cost an instruction: x + 0 is not x for x = -0)
+    const float part = (s[kb][base + 0] + s[kb][base + 1]) + (s[kb][base + 2] + s[kb][base + 3]);
+    xsum[half] = cc == 0 ? part : xsum[half] + part;
     uint32_t r0 = w0, r1 = w1;
     pin(r0);
     pin(r1);
@@ -516,7 +524,11 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
     constexpr int NP = 2 * NCC;  // p slices (4 scores each)
     constexpr int SLOTS = NSA > NP ? NSA : NP;
     static_assert(PFB <= SLOTS && PFA <= NSA, "prefetch depths");
-    lsum[0] = lsum[1] = xsum[0] = xsum[1] = 0.0f;
+    // the exponentials make this the VALU-heavy phase: it gets issue priority
+    // over the other wave on the SIMD, which is then typically in its
+    // MFMA-heavy phase B
+    __builtin_amdgcn_s_setprio(1);
+    lsum[0] = lsum[1] = 0.0f;
     u32x4 kf[RKA];
 #pragma unroll
     for (int k = 0; k < PFA; ++k) kf[k % RKA] = kfrag(Kt, k);
@@ -541,6 +553,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
     }
     l += lsum[0] + lsum[1];
     lx += xsum[0] + xsum[1];
+    __builtin_amdgcn_s_setprio(0);
   };
   // phase B of iteration j: value MFMAs of tile j (V^T from Vt, P^T in pf;
   // fragments 0 .. PFB-1 already requested in phase A) beside the reference
