@@ -1,7 +1,7 @@
 // Exact attention forward for CDNA4 (gfx950): one workgroup per (batch, head,
-// query block of 256 rows in bf16, 128 in fp32), online softmax over 64-key
-// (bf16) or 32-key (fp32) tiles held in LDS, both contractions on MFMA with
-// fp32 accumulators.
+// query block of 128 rows), online softmax over 64-key (16-bit inputs) or
+// 32-key (fp32) tiles held in LDS, both contractions on MFMA with fp32
+// accumulators.
 //
 // The method is the tiled loop of "Flash Attention" (wiki.ai-engineering.at),
 // section "Tiling Algorithm" — an outer loop over query blocks, an inner loop
@@ -15,21 +15,21 @@
 // Inferenz?", section "Kernel-Fusion hält mehr Schritte der Attention-Kette in
 // einem Ausführungspfad"); only Q, K, V are read and only O and LSE written.
 //
-// Layout of the work (bf16):
-//   * 8 waves x 32 query rows.  Each wave computes S^T = K Q^T with
-//     v_mfma_f32_32x32x16_bf16: keys on the MFMA rows, queries on the lanes.
-//     A lane then holds 16 scores of ONE query per 32-key block, so the row
-//     max is an in-register reduction plus one exchange with lane^32, and
-//     the rescale factor of the output is a per-lane scalar.
+// Layout of the work (16-bit inputs):
+//   * 4 waves x 32 query rows.  Each wave computes S^T = K Q^T with
+//     v_mfma_f32_32x32x16_bf16 (or _f16): keys on the MFMA rows, queries on
+//     the lanes.  A lane then holds 16 scores of ONE query per 32-key block, so
+//     the row max is an in-register reduction plus one exchange with lane^32,
+//     and the rescale factor of the output is a per-lane scalar.
 //   * O^T = V^T P^T with the same MFMA: P^T is the B operand straight from the
-//     score registers (converted to bf16); V^T comes from LDS.  To make the
-//     eight keys a lane holds for one MFMA consecutive, the K rows of the
-//     score MFMA are permuted (bits 2 and 3 of the row index swapped); V^T is
-//     then read in natural key order.
-//   * K tiles are stored row-major in LDS with the 16-byte chunk index XORed by
-//     the row, V tiles transposed (V^T, [d][key]) with a chunk XOR by d, so the
-//     MFMA operand reads of 32 different rows hit distinct banks.  Tiles are
-//     double buffered and loaded while the previous tile is consumed.
+//     score registers (rounded to 16 bits); V^T is read from the row-major V
+//     tile with the transposing LDS read.  To make the eight keys a lane holds
+//     for one MFMA consecutive, the K rows of the score MFMA are permuted (bits
+//     2 and 3 of the row index swapped); V^T is then read in natural key order.
+//   * K and V tiles are stored row-major in LDS with the 16-byte chunk index
+//     XORed by a function of the row, so the MFMA operand reads of 32 different
+//     rows hit distinct banks.  Tiles are double buffered and loaded (global to
+//     LDS, no registers) while the previous tile is consumed.
 //   * The running reference max moves only when a row's tile max exceeds it by
 //     more than kTau (log2 units), so the output rescale is rare; the final
 //     o / l and LSE = (m + log2 l) ln 2 are exact for any reference <= max.
