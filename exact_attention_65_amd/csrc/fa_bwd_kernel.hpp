@@ -164,10 +164,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
   const int N = a.n;
-  const int t = xcd_remap(blockIdx.x, a.n_blocks);
-  const int bh = t / a.n_blk;
-  int qb = t - bh * a.n_blk;
-  if (CAUSAL) qb = a.n_blk - 1 - qb;  // longest query blocks first
+  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL);
+  const int bh = wi.bh;
+  const int qb = CAUSAL ? a.n_blk - 1 - wi.idx : wi.idx;  // causal: longest query blocks first
   const int q0 = qb * kBwdRows;
   const size_t head = (size_t)bh * N * D;
   const uint16_t* Qg = (const uint16_t*)a.q + head;
@@ -362,9 +361,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
   const int N = a.n;
-  const int t = xcd_remap(blockIdx.x, a.n_blocks);
-  const int bh = t / a.n_blk;
-  const int kblk = t - bh * a.n_blk;  // causal: the first key blocks see the most queries
+  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL);
+  const int bh = wi.bh;
+  const int kblk = wi.idx;  // causal: the first key blocks see the most queries
   const int k0 = kblk * kBwdRows;
   const size_t head = (size_t)bh * N * D;
   const uint16_t* Qg = (const uint16_t*)a.q + head;

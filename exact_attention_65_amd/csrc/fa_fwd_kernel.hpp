@@ -89,6 +89,31 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return base + j;
 }
 
+// Work item t (after xcd_remap) of a grid of n_bh heads x per_bh items: its
+// head and its index within the head.  Plain order: a head's items one after
+// another.  Interleaved order (for the causal mask, where item 0 of a head is
+// its longest): when n_bh is a multiple of 8, each XCD holds n_bh/8 whole heads
+// and takes them in groups of up to 4, the items of a group round-robin over
+// its heads.  Each XCD then starts all its long items first; head by head, the
+// long items of the last heads on an XCD would start after the short items of
+// the others and end late.  Groups of at most 4 heads keep the K/V bytes in
+// use on an XCD at a few heads' worth.
+struct HeadItem {
+  int bh, idx;
+};
+__device__ __forceinline__ HeadItem head_item(int t, int n_bh, int per_bh, bool interleave) {
+  if (interleave && (n_bh & 7) == 0) {
+    const int hp = n_bh >> 3;                                       // heads per XCD
+    const int g = hp <= 4 ? hp : (hp & 3) == 0 ? 4 : (hp & 1) == 0 ? 2 : 1;  // heads per group
+    const int per_x = hp * per_bh;  // = n_blocks / 8: xcd_remap gives XCD x the items [x per_x, (x+1) per_x)
+    const int x = t / per_x, j = t - x * per_x;
+    const int grp = j / (g * per_bh), jj = j - grp * (g * per_bh);
+    return {x * hp + grp * g + jj % g, jj / g};
+  }
+  const int bh = t / per_bh;
+  return {bh, t - bh * per_bh};
+}
+
 // Row i of a 32-row MFMA block holds key swap23(i): swaps bits 2 and 3.
 __device__ __forceinline__ int swap23(int i) {
   return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
@@ -313,14 +338,13 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   // query i is position i + OFF of the sequence: key j is visible iff j <= i + OFF
   const int OFF = CAUSAL ? NK - NQ : 0;
 
-  // workgroup -> (b, h), query block, key range; consecutive ids share (b, h)
-  const int t = xcd_remap(blockIdx.x, a.n_blocks);
-  const int per_bh = a.n_qblk * a.n_split;
-  const int bh = t / per_bh;
-  const int rem = t - bh * per_bh;
-  int qb = SPLIT ? rem / a.n_split : rem;
-  const int split = SPLIT ? rem - qb * a.n_split : 0;
-  if (CAUSAL) qb = a.n_qblk - 1 - qb;  // longest query blocks first
+  // workgroup -> (b, h), query block, key range; under the causal mask the
+  // longest query blocks first
+  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_bh, a.n_qblk * a.n_split, CAUSAL);
+  const int bh = wi.bh;
+  int qb = SPLIT ? wi.idx / a.n_split : wi.idx;
+  const int split = SPLIT ? wi.idx - qb * a.n_split : 0;
+  if (CAUSAL) qb = a.n_qblk - 1 - qb;
   const int q0 = qb * kBF16Rows;
   const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + (size_t)bh * NQ * D;
   const uint16_t* __restrict__ Kg = (const uint16_t*)a.k + (size_t)bh * NK * D;
@@ -760,10 +784,9 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fa_fwd_f32_kernel(
   const int h = lane >> 5, c32 = lane & 31;
   const int N = a.nq;  // the fp32 path has as many queries as keys
 
-  const int t = xcd_remap(blockIdx.x, a.n_blocks);
-  const int bh = t / a.n_qblk;
-  int qb = t - bh * a.n_qblk;
-  if (CAUSAL) qb = a.n_qblk - 1 - qb;
+  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_bh, a.n_qblk, CAUSAL);
+  const int bh = wi.bh;
+  const int qb = CAUSAL ? a.n_qblk - 1 - wi.idx : wi.idx;  // causal: longest query blocks first
   const int q0 = qb * kBM;
   const size_t head = (size_t)bh * (size_t)N * D;
   const float* __restrict__ Qg = (const float*)a.q + head;
