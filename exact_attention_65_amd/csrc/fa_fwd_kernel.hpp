@@ -300,9 +300,9 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   typedef typename E::vec8 vec8;
   constexpr int BN = 64;                // keys per tile
   // D = 96 rows are stored in LDS as 128-wide rows whose last 4 chunks stay
-  // zero (so are Q's columns 96 .. 127): every LDS address and MFMA step is
-  // the D = 128 one; global rows keep their real width
-  constexpr int DP = D == 96 ? 128 : D; // head dimension of the LDS layout and the MFMAs
+  // zero: every LDS address is the D = 128 one (same swizzles); global rows
+  // keep their real width
+  constexpr int DP = D == 96 ? 128 : D; // head dimension of the LDS layout
   constexpr int GRB = D * 2;            // bytes per global K / V row
   constexpr int RB = DP * 2;            // bytes per LDS K / V row
   constexpr int CPR = DP / 8;           // 16-byte chunks per LDS row
@@ -310,15 +310,17 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   constexpr int TILE16 = BN * CPR;      // 16-byte chunks per tile
   constexpr int NLD = TILE16 / 64 / 4;  // 1 KB K loads per wave per tile
   constexpr int NKB = BN / 32;          // 32-key MFMA blocks per tile
-  constexpr int NDB = DP / 32;          // 32-wide d blocks of O
-  constexpr int NKK = DP / 16;          // 16-deep steps of the score contraction
+  // the MFMAs cover the D real columns only (at D = 96 the padded LDS columns
+  // are never read)
+  constexpr int NDB = D / 32;           // 32-wide d blocks of O
+  constexpr int NKK = D / 16;           // 16-deep steps of the score contraction
   constexpr int NCC = BN / 16;          // 16-key steps of the value contraction
   constexpr int NSA = NKK * NKB;        // score MFMAs per tile (phase A slots)
   constexpr int NSB = NDB * NCC;        // value MFMAs per tile (phase B slots)
   constexpr int PFA = 3;                // score-fragment reads in flight in phase A
   constexpr int PFB = 4;                // value-fragment reads in flight in phase B
   static_assert(NLD >= 1, "tile loads");
-  static_assert(NSA == 2 * DP / 16 && NSB == DP / 8, "slot counts");
+  static_assert(NSA == 2 * D / 16 && NSB == D / 8, "slot counts");
   // fragment arrays: one entry per slot, or at D = 256 (32 slots a phase) a
   // ring of PF + 1 entries, which the compiler keeps in registers where it
   // puts a 32-entry array in scratch memory
