@@ -62,8 +62,9 @@ typedef enum fa_status {
   FA_ERR_BAD_DTYPE = 4,    /* dtype is not one of fa_dtype                            */
   FA_ERR_MISALIGNED = 5,   /* a pointer is not 16-byte aligned                        */
   FA_ERR_ALIASING = 6,     /* o or lse overlaps q, k, v or each other                 */
-  FA_ERR_UNSUPPORTED = 7,  /* valid but not built: D not 64/128, N*D >= 2^31, more   */
-                           /* than 2^31-1 workgroups, or the device is not gfx950     */
+  FA_ERR_UNSUPPORTED = 7,  /* valid but not built: a head dimension or dtype the     */
+                           /* entry point lacks, N*D >= 2^31, more than 2^31-1        */
+                           /* workgroups, or the device is not gfx950                 */
   FA_ERR_HIP = 8,          /* a HIP runtime call failed (no device, launch failure)   */
   FA_ERR_WORKSPACE = 9     /* workspace_bytes below what the call needs               */
 } fa_status;
@@ -83,8 +84,9 @@ typedef struct fa_sizes {
  *
  * Pure host function: needs no device and touches no HIP state.  Fills *out
  * whenever the shape and dtype are valid, then returns FA_OK when fa_fwd
- * supports the shape, FA_ERR_UNSUPPORTED when it does not (D not in {64, 128},
- * N*D >= 2^31, or more than 2^31-1 workgroups), FA_ERR_BAD_SHAPE /
+ * supports the shape, FA_ERR_UNSUPPORTED when it does not (D not in {64, 128}
+ * for float32 or {64, 96, 128, 256} for bfloat16 and float16, N*D >= 2^31, or
+ * more than 2^31-1 workgroups), FA_ERR_BAD_SHAPE /
  * FA_ERR_BAD_DTYPE for invalid arguments and FA_ERR_NULL_POINTER if out is
  * NULL.  The device architecture is not checked here.
  */
@@ -137,11 +139,12 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * the library's choice, which depends only on the arguments: enough ranges
  * for about 512 workgroups, but at least 8 key tiles of 64 per range, at most
  * Nk / (4 Nq) ranges (partial results within a quarter of the K/V bytes) and at
- * most 64; so one range unless the queries are few against many keys.  *out and *splits_out are written only on FA_OK.
+ * most 64; so one range unless the queries are few against many keys.
+ * *out and *splits_out are written only on FA_OK.
  * Returns FA_OK, FA_ERR_BAD_SHAPE (a size <= 0, Nq > Nk with
  * causal, n_splits outside 0..FA_SPLIT_MAX, overflow), FA_ERR_BAD_DTYPE,
  * FA_ERR_NULL_POINTER (out NULL) or FA_ERR_UNSUPPORTED (float32, D not in
- * {64, 128}, Nq*D or Nk*D >= 2^31, more than 2^31-1 workgroups).
+ * {64, 96, 128, 256}, Nq*D or Nk*D >= 2^31, more than 2^31-1 workgroups).
  */
 fa_status fa_fwd_split_query(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
                              int n_splits, fa_dtype dtype, fa_sizes* out, int* splits_out);
