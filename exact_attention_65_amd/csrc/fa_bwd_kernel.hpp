@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
   const int N = a.n;
-  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL);
+  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL, true);
   const int bh = wi.bh;
   const int qb = CAUSAL ? a.n_blk - 1 - wi.idx : wi.idx;  // causal: longest query blocks first
   const int q0 = qb * kBwdRows;
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
   const int N = a.n;
-  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL);
+  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL, false);
   const int bh = wi.bh;
   const int kblk = wi.idx;  // causal: the first key blocks see the most queries
   const int k0 = kblk * kBwdRows;

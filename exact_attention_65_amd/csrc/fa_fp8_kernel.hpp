@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kFp8Threads, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
   const int N = a.n;
-  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_blocks / a.n_qblk, a.n_qblk, CAUSAL);
+  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_blocks / a.n_qblk, a.n_qblk, CAUSAL, true);
   const int bh = wi.bh;
   const int qb = CAUSAL ? a.n_qblk - 1 - wi.idx : wi.idx;  // causal: longest query blocks first
   const int q0 = qb * kFp8Rows;

@@ -98,15 +98,30 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 // long items of the last heads on an XCD would start after the short items of
 // the others and end late.  Groups of at most 4 heads keep the K/V bytes in
 // use on an XCD at a few heads' worth.
+//
+// For kernels that run two workgroups per CU (two_per_cu): when an XCD has
+// more items than CUs but at most two per CU (32 < items <= 64 on MI355X's 32
+// CUs per XCD), every item starts at once, and the dispatcher places item
+// positions c and c + 32 on CU c.  An item that shares its CU runs slower than
+// one alone, so the longest items get CUs of their own and the others share
+// CUs longest with shortest.
+constexpr int kCusPerXcd = 32;
+__device__ __forceinline__ int pair_rank(int p, int n) {
+  if (n <= kCusPerXcd || n > 2 * kCusPerXcd) return p;
+  const int shared = n - kCusPerXcd;               // CUs 0 .. shared-1 hold two items
+  if (p >= kCusPerXcd) return n - 1 - (p - kCusPerXcd);  // second item of CU p-32: the shortest
+  return p >= shared ? p - shared : (kCusPerXcd - shared) + p;
+}
+
 struct HeadItem {
   int bh, idx;
 };
-__device__ __forceinline__ HeadItem head_item(int t, int n_bh, int per_bh, bool interleave) {
+__device__ __forceinline__ HeadItem head_item(int t, int n_bh, int per_bh, bool interleave, bool two_per_cu) {
   if (interleave && (n_bh & 7) == 0) {
     const int hp = n_bh >> 3;                                       // heads per XCD
     const int g = hp <= 4 ? hp : (hp & 3) == 0 ? 4 : (hp & 1) == 0 ? 2 : 1;  // heads per group
     const int per_x = hp * per_bh;  // = n_blocks / 8: xcd_remap gives XCD x the items [x per_x, (x+1) per_x)
-    const int x = t / per_x, j = t - x * per_x;
+    const int x = t / per_x, j = two_per_cu ? pair_rank(t - x * per_x, per_x) : t - x * per_x;
     const int grp = j / (g * per_bh), jj = j - grp * (g * per_bh);
     return {x * hp + grp * g + jj % g, jj / g};
   }
@@ -342,7 +357,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
 
   // workgroup -> (b, h), query block, key range; under the causal mask the
   // longest query blocks first
-  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_bh, a.n_qblk * a.n_split, CAUSAL);
+  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_bh, a.n_qblk * a.n_split, CAUSAL, D != 256);
   const int bh = wi.bh;
   int qb = SPLIT ? wi.idx / a.n_split : wi.idx;
   const int split = SPLIT ? wi.idx - qb * a.n_split : 0;
@@ -786,7 +801,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fa_fwd_f32_kernel(
   const int h = lane >> 5, c32 = lane & 31;
   const int N = a.nq;  // the fp32 path has as many queries as keys
 
-  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_bh, a.n_qblk, CAUSAL);
+  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_bh, a.n_qblk, CAUSAL, D != 128);
   const int bh = wi.bh;
   const int qb = CAUSAL ? a.n_qblk - 1 - wi.idx : wi.idx;  // causal: longest query blocks first
   const int q0 = qb * kBM;
