@@ -53,16 +53,20 @@ BWD_FLOP_FACTOR = 2.5  # five N x N x D products against the forward's two
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_bf16_d128_b2_h32_n4096.txt")
 
 
+def code_only(src: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_hash() -> str:
     """Hash of the kernel sources with comments and whitespace removed, so that an
     edit of comments alone keeps the counter summary valid."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), encoding="utf-8") as f:
-            src = f.read()
-        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-        src = re.sub(r"//[^\n]*", " ", src)
-        h.update(" ".join(src.split()).encode())
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,0 +1,42 @@
+"""Host-side parts of bench.py (no GPU): the one-GPU refusal, the hash that ties
+the committed counter summary to the kernel source, and the CPU-baseline record."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+import fa_inputs as fi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+def test_code_only_ignores_comments_and_whitespace_but_not_code():
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* the\n result */\n}\n"
+    b = "int f(int x) {\n\treturn 2 * x;\n}"
+    c = "int f(int x) { return 3 * x; }"
+    assert bench.code_only(a) == bench.code_only(b)
+    assert bench.code_only(a) != bench.code_only(c)
+
+
+def test_traffic_record_is_read_only_for_its_workload():
+    # another workload never picks up the headline kernel's counter summary
+    assert bench.read_traffic("bf16_causal_b1_h32_n4096_d128") is None
+    v = bench.read_traffic("bf16_b2_h32_n4096_d128")
+    # present exactly when the summary was taken for the kernel source as it stands
+    assert v is None or v > 0
+
+
+def test_cpu_baseline_record():
+    rec = bench.cpu_baseline(fi.FP32_SMALL, budget_s=0.01)
+    assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
+    assert rec["value"] > 0 and rec["cores"] >= 1
+    assert rec["sample"].startswith("1 of 1 (b,h) heads of " + fi.FP32_SMALL.name)
