@@ -1,9 +1,12 @@
-"""Host-side parts of bench.py (no GPU): the one-GPU refusal, the hash that ties
-the committed counter summary to the kernel source, and the CPU-baseline record."""
+"""bench.py: on the host, the one-GPU refusal, the hash that ties the committed
+counter summary to the kernel source and the CPU-baseline record; on the GPU, one
+short run whose JSON line carries every field of the benchmark contract."""
 import json
 import os
 import subprocess
 import sys
+
+import pytest
 
 import bench
 import fa_inputs as fi
@@ -40,3 +43,21 @@ def test_cpu_baseline_record():
     assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
     assert rec["value"] > 0 and rec["cores"] >= 1
     assert rec["sample"].startswith("1 of 1 (b,h) heads of " + fi.FP32_SMALL.name)
+
+
+@pytest.mark.gpu
+def test_bench_line_on_the_gpu():
+    """One short bench.py run: the JSON line carries the contract's fields."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", fi.FP32_SMALL.name,
+                        "--steps", "3", "--warmup", "1"], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["value"] > 0
+    assert d["config"]["workload"] == fi.FP32_SMALL.name
+    rf = d["roofline"]
+    assert rf["bound"] in ("mfma", "hbm") and rf["achieved"] > 0 and rf["peak"] > 0
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["cores"] >= 1
