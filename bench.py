@@ -128,6 +128,40 @@ def cpu_baseline(w, budget_s: float = 12.0, backward: bool = False):
                       f"({t_total:.2f} s)"}
 
 
+def naive_context(q, k, v, w, fa_ms, stream, reps: int = 10):
+    """Plain torch attention on the same inputs: S = scale Q K^T and P = softmax(S)
+    materialised in device memory (the N x N round trip the tiled method avoids),
+    then O = P V; both products in the input dtype with the library's fp32
+    accumulation, the softmax in fp32.  Reported as context, never as a target."""
+    import torch
+    kt = k.transpose(-2, -1).contiguous()  # batched 16-bit products take a contiguous right operand
+    mask = None
+    if w.causal:
+        mask = torch.ones(w.N, w.N, dtype=torch.bool, device=q.device).triu(1)
+
+    def naive():
+        s = torch.matmul(q, kt).float() * w.scale
+        if mask is not None:
+            s.masked_fill_(mask, float("-inf"))
+        p = torch.softmax(s, dim=-1).to(q.dtype)
+        del s
+        return torch.matmul(p, v)
+
+    naive()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        naive()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del kt, mask
+    torch.cuda.empty_cache()
+    return {"kind": "plain torch attention (matmul, fp32 softmax, matmul), same GPU and inputs",
+            "ms_per_call": round(ms, 4), "ratio_to_fa": round(ms / fa_ms, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +174,9 @@ def main():
                     help="time fa_bwd (the gradients) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="one line per workload instead of the headline")
+    ap.add_argument("--naive-context", action="store_true",
+                    help="also time plain torch attention (matmul, softmax, matmul with the N x N scores in "
+                         "device memory) on the same inputs, as context only")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 times), the known-size "
                          "reference that scales the HBM byte counters")
@@ -316,6 +353,8 @@ def main():
                        "launch_ms_median": round(float(np.median(launch_ms)), 5)},
             "roofline": roofline,
         }
+        if args.naive_context and w.dtype in ("bf16", "f16") and not args.backward and split is None:
+            rec["context"] = naive_context(q, k, v, w, ms_per_step, stream)
         if not args.no_cpu_baseline and not args.sweep:
             del q, k, v, o, lse
             torch.cuda.empty_cache()
