@@ -473,9 +473,14 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   f32x16 sA[NKB], sB[NKB];
   vec8 pf[NCC];
   float m_ref = neg_inf(), l = 0.0f, lx = 0.0f, mu = 0.0f;
+  // raw tile maxima above thr move the reference: c thr = m_ref + kTau (-inf
+  // until a key is seen; +inf when that overflows, at the smallest c, where
+  // every c s is too small to move it)
+  float thr = neg_inf();
   bool pend = false;
   float pend_alpha = 1.0f;
   const float c = a.c;
+  const float c_inv = 1.0f / c;
 
   // ---- pieces of the softmax -------------------------------------------
   // mask keys past the workgroup's key range (past NK, or in the next
@@ -512,20 +517,25 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
 #pragma unroll
       for (int kb = 1; kb < NKB; ++kb) mx = vmax(mx, mpart[kb]);
       mx = pair_max(mx);
-      const float mt = mx * c;
-      const bool any = __builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0;
-      const float m_new = any ? vmax(m_ref, mt) : m_ref;
-      const float alpha = m_new == neg_inf() ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      l *= alpha;
-      lx *= alpha;
-      m_ref = m_new;
-      pend = any;
-      pend_alpha = alpha;
-      mu = m_new == neg_inf() ? 0.0f : m_new;
+      // wave-uniform branch: the update runs only when a row's tile max
+      // exceeds its reference by more than kTau (rare after the first tiles);
+      // then every row takes the larger of its reference and its tile max
+      if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
+        const float m_new = vmax(m_ref, mx * c);
+        const float alpha = m_new == neg_inf() ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        l *= alpha;
+        lx *= alpha;
+        m_ref = m_new;
+        pend = true;
+        pend_alpha = alpha;
+        mu = m_new == neg_inf() ? 0.0f : m_new;
+        thr = (m_new + kTau) * c_inv;
+      }
       pin(mu);
       pin(pend_alpha);
       pin(l);
       pin(lx);
+      pin(thr);
     }
   };
   // p = exp2(c s - mu) for the 8 scores of value step cc, their sums, and the
