@@ -480,7 +480,6 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   bool pend = false;
   float pend_alpha = 1.0f;
   const float c = a.c;
-  const float c_inv = 1.0f / c;
 
   // ---- pieces of the softmax -------------------------------------------
   // mask keys past the workgroup's key range (past NK, or in the next
@@ -529,7 +528,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
         pend = true;
         pend_alpha = alpha;
         mu = m_new == neg_inf() ? 0.0f : m_new;
-        thr = (m_new + kTau) * c_inv;
+        thr = (m_new + kTau) / c;  // a division in the rare path: no register for 1/c
       }
       pin(mu);
       pin(pend_alpha);
