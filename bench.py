@@ -211,8 +211,8 @@ def main():
         split = args.split if args.split is not None else (fa.FA_SPLIT_AUTO if w.NQ > 0 else None)
         if args.backward:
             split = None
-            if w.dtype != "bf16" or w.NQ > 0 or w.D not in (64, 128):
-                continue  # the gradients take bf16, square shapes and D in {64, 128}
+            if w.dtype not in ("bf16", "f16") or w.NQ > 0 or w.D not in (64, 128):
+                continue  # the gradients take bf16 or fp16, square shapes and D in {64, 128}
         if w.dtype == "fp8":
             split = None
         if split is not None and w.dtype not in ("bf16", "f16"):
@@ -250,7 +250,8 @@ def main():
 
         if args.backward:
             bits = fi.full_tensor(w, fi.T_DO)
-            do = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+            do = (torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16"
+                  else torch.from_numpy(bits.view(np.float16))).cuda()
             del bits
             fa.attention_forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
             grads = [torch.empty_like(q) for _ in range(3)]

@@ -243,15 +243,17 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
                        dq=None, dk=None, dv=None, workspace=None, stream=None):
     """dq, dk, dv of attention_forward's o for the upstream gradient dout.
 
-    q, k, v, o, dout: contiguous bf16 GPU tensors [B, H, N, D]; o and lse as
+    q, k, v, o, dout: contiguous bf16 or fp16 GPU tensors [B, H, N, D] of one
+    dtype (the gradients have it too); o and lse as
     attention_forward returned them for the same q, k, v, causal and scale.
     Allocates the gradients (and the workspace, unless a uint8 GPU tensor is
     given) with torch.  Launches on ``stream`` (default: torch's current
     stream); no synchronisation.
     """
     import torch
-    if q.dtype != torch.bfloat16:
+    if q.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError(f"unsupported dtype {q.dtype}")
+    dt = _dtype_code(q.dtype)
     for x in (q, k, v, o, dout):
         if x.dtype != q.dtype or x.shape != q.shape or not x.is_cuda or not x.is_contiguous():
             raise ValueError("q, k, v, o, dout must be contiguous GPU tensors of one shape and dtype")
@@ -260,7 +262,7 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    st, sz = fa_bwd_query(B, H, N, D, causal, FA_DTYPE_BF16)
+    st, sz = fa_bwd_query(B, H, N, D, causal, dt)
     if st != FA_OK:
         raise FaError(st)
     dq = torch.empty_like(q) if dq is None else dq
@@ -272,7 +274,7 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
         stream = torch.cuda.current_stream(q.device)
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                workspace.numel() * workspace.element_size(), B, H, N, D, causal, scale, FA_DTYPE_BF16,
+                workspace.numel() * workspace.element_size(), B, H, N, D, causal, scale, dt,
                 stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st)

@@ -23,16 +23,23 @@ hipError_t launch(Kern kern, const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(int D, bool causal, BwdArgs a, float scale, hipStream_t s) {
-  // dq kernel: Q's signs carry the sign of scale
+template <typename E>
+hipError_t launch_bwd_typed(int D, bool causal, BwdArgs a, float scale, hipStream_t s) {
+  // dq kernel: Q's signs carry the sign of scale (the sign bit of both 16-bit types is bit 15)
   a.flip = std::signbit(scale) && scale != 0.0f ? 0x80008000u : 0u;
   hipError_t e;
-  if (D == 128) e = causal ? launch(fa_bwd_dq_kernel<128, true>, a, s) : launch(fa_bwd_dq_kernel<128, false>, a, s);
-  else e = causal ? launch(fa_bwd_dq_kernel<64, true>, a, s) : launch(fa_bwd_dq_kernel<64, false>, a, s);
+  if (D == 128) e = causal ? launch(fa_bwd_dq_kernel<E, 128, true>, a, s) : launch(fa_bwd_dq_kernel<E, 128, false>, a, s);
+  else e = causal ? launch(fa_bwd_dq_kernel<E, 64, true>, a, s) : launch(fa_bwd_dq_kernel<E, 64, false>, a, s);
   if (e != hipSuccess) return e;
   // dkdv kernel: K's signs carry it
-  if (D == 128) return causal ? launch(fa_bwd_dkdv_kernel<128, true>, a, s) : launch(fa_bwd_dkdv_kernel<128, false>, a, s);
-  return causal ? launch(fa_bwd_dkdv_kernel<64, true>, a, s) : launch(fa_bwd_dkdv_kernel<64, false>, a, s);
+  if (D == 128)
+    return causal ? launch(fa_bwd_dkdv_kernel<E, 128, true>, a, s) : launch(fa_bwd_dkdv_kernel<E, 128, false>, a, s);
+  return causal ? launch(fa_bwd_dkdv_kernel<E, 64, true>, a, s) : launch(fa_bwd_dkdv_kernel<E, 64, false>, a, s);
+}
+
+hipError_t launch_bwd(int dtype, int D, bool causal, const BwdArgs& a, float scale, hipStream_t s) {
+  return dtype == FA_DTYPE_F16 ? launch_bwd_typed<F16>(D, causal, a, scale, s)
+                               : launch_bwd_typed<BF16>(D, causal, a, scale, s);
 }
 
 }  // namespace
@@ -65,5 +72,6 @@ extern "C" __attribute__((visibility("default"))) fa_status fa_bwd(
   a.c = c < FLT_MIN ? FLT_MIN : c;
   a.scale = scale;
   a.flip = 0u;
-  return fa::launch_bwd((int)D, causal != 0, a, scale, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  const hipError_t e = fa::launch_bwd((int)dtype, (int)D, causal != 0, a, scale, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -1,4 +1,4 @@
-// Gradients of the exact attention forward for CDNA4 (gfx950), bf16 inputs.
+// Gradients of the exact attention forward for CDNA4 (gfx950), bf16 or fp16 inputs.
 //
 // The pages say only that a second pass computes the gradients over the same
 // chunks without storing the score matrix ("Flash Attention: ускорить
@@ -14,8 +14,10 @@
 //   fa_bwd_dkdv_kernel  one workgroup per 128 keys, Q and dO tiles streamed:
 //                       S = Q K^T, dP = dO V^T, then dV^T += dO^T P and
 //                       dK^T += Q^T dS.
-// Every contraction runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulators; P
-// and dS are rounded to bf16 as MFMA operands, outputs to bf16 once.
+// Every contraction runs on the 32x32x16 MFMA of the input type (bf16 or fp16)
+// with fp32 accumulators; P and dS are rounded to that type as MFMA operands,
+// the outputs once.  The kernels are templates over the element type E (BF16 or
+// F16, the forward's element-type structs).
 #pragma once
 
 #include "fa_fwd_kernel.hpp"
@@ -65,7 +67,7 @@ __device__ __forceinline__ int bswz(int row) {
   }
 }
 
-// Byte offset of 16-byte chunk `chunk` of tile row `row` (rows of D bf16).
+// Byte offset of 16-byte chunk `chunk` of tile row `row` (rows of D 16-bit elements).
 template <int D>
 __device__ __forceinline__ uint32_t chunk_addr(int row, int chunk) {
   return (uint32_t)(row * D * 2 + ((chunk ^ bswz<D>(row)) * 16));
@@ -108,39 +110,40 @@ __device__ __forceinline__ u32x4 tr_frag(const u32x4* t, uint32_t tb0, uint32_t 
 
 // Row of the operand held in registers: [row][16kk + 8h .. +7] as MFMA B
 // fragments, signs flipped by `flip`, zero for rows past N.
-template <int NKK>
-__device__ __forceinline__ void load_row(bf16x8 (&f)[NKK], const uint16_t* g, int row, int N, int D, int h,
+template <typename V, int NKK>
+__device__ __forceinline__ void load_row(V (&f)[NKK], const uint16_t* g, int row, int N, int D, int h,
                                          uint32_t flip) {
   const u32x4 fl = {flip, flip, flip, flip};
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     u32x4 x = {0u, 0u, 0u, 0u};
     if (row < N) x = *(const u32x4*)(g + (size_t)row * D + 16 * kk + 8 * h) ^ fl;
-    f[kk] = __builtin_bit_cast(bf16x8, x);
+    f[kk] = __builtin_bit_cast(V, x);
   }
 }
 
-// Pack 8 consecutive fp32 values of an accumulator into one bf16x8 operand.
-__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
+// Pack 8 consecutive fp32 values of an accumulator into one 16-bit operand.
+template <typename E>
+__device__ __forceinline__ typename E::vec8 pack8(const f32x16& s, int base) {
   // scalars first: this compiler miscompiles __builtin_bit_cast of a vector element
   uint32_t w[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = pack_bf16(s[base + 2 * e], s[base + 2 * e + 1]);
+  for (int e = 0; e < 4; ++e) w[e] = E::pack(s[base + 2 * e], s[base + 2 * e + 1]);
   const u32x4 x = {w[0], w[1], w[2], w[3]};
-  return __builtin_bit_cast(bf16x8, x);
+  return __builtin_bit_cast(typename E::vec8, x);
 }
 
 // Store a [D x 32] MFMA accumulator (rows d, this lane's column = one row of
-// the output) as bf16 after multiplying by mul.
-template <int NDB>
+// the output) in the 16-bit type after multiplying by mul.
+template <typename E, int NDB>
 __device__ __forceinline__ void store_rows(uint16_t* out_row, const f32x16 (&acc)[NDB], int h, float mul) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = 32 * db + 8 * g + 4 * h;
-      const u32x2 w = {pack_bf16(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul),
-                       pack_bf16(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+      const u32x2 w = {E::pack(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul),
+                       E::pack(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
       *(u32x2*)(out_row + d) = w;
     }
 }
@@ -154,8 +157,9 @@ __device__ __forceinline__ void store_rows(uint16_t* out_row, const f32x16 (&acc
 // the columns: the forward's orientation), 16 MFMAs dP^T = V dO^T, the
 // elementwise dS^T = P^T (dP^T - Delta), and 16 MFMAs dQ^T += K^T dS^T with
 // K^T read transposed from the same tile (for D = 128; half as many for 64).
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
+  typedef typename E::vec8 vec8;
   constexpr int BN = 64, RB = D * 2, CPR = D / 8, RPB = 64 / CPR, TILE16 = BN * CPR;
   constexpr int NLD = TILE16 / 64 / 4, NKB = BN / 32, NDB = D / 32, NKK = D / 16, NCC = BN / 16;
   __shared__ u32x4 kA[TILE16], kB[TILE16], vA[TILE16], vB[TILE16];
@@ -188,12 +192,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
 
   // this lane's query row: Q (signs flipped for a negative scale) and dO as MFMA
   // B fragments; Delta = sum_d dO O (each half-wave holds half the d's)
-  bf16x8 qf[NKK], dof[NKK];
+  vec8 qf[NKK], dof[NKK];
   bwd::load_row(qf, Qg, qrow, N, D, h, a.flip);
   bwd::load_row(dof, dOg, qrow, N, D, h, 0u);
   float dsum = 0.0f;
   {
-    bf16x8 of[NKK];
+    vec8 of[NKK];
     bwd::load_row(of, Og, qrow, N, D, h, 0u);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -201,8 +205,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t xe = x[e], ye = y[e];
-        dsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xe), __builtin_bit_cast(bf16x2, ye),
-                                               dsum, false);
+        dsum = E::dot2(xe, ye, dsum);
       }
     }
   }
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
     const int kv0 = j * BN;
     const bool masked = kv0 + BN > N || (CAUSAL && kv0 + BN - 1 > wave_q0);
     f32x16 s[NKB], dp[NKB];
-    bf16x8 dsf[NCC];
+    vec8 dsf[NCC];
     // element (kb, i) holds key kv0 + 32kb + 8h + kofs(i) of query qrow
     auto mask_block = [&](int kb) __attribute__((always_inline)) {
       if (masked) {
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
       float ds = p * (dp[kb][i] - delta);
       pin(ds);
       s[kb][i] = ds;
-      if ((i & 7) == 7) dsf[2 * kb + (i >> 3)] = bwd::pack8(s[kb], i & 8);
+      if ((i & 7) == 7) dsf[2 * kb + (i >> 3)] = bwd::pack8<E>(s[kb], i & 8);
     };
     u32x4 sf[NSS], gf[NSG];
 #pragma unroll
@@ -282,11 +285,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
       const int kb = k / (2 * NKK), kk = (k / 2) % NKK;
       const f32x16 z = {};
       if (k & 1)
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sf[k]), dof[kk],
-                                                         kk == 0 ? z : dp[kb], 0, 0, 0);
+        dp[kb] = E::mfma(__builtin_bit_cast(vec8, sf[k]), dof[kk], kk == 0 ? z : dp[kb]);
       else
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sf[k]), qf[kk],
-                                                        kk == 0 ? z : s[kb], 0, 0, 0);
+        s[kb] = E::mfma(__builtin_bit_cast(vec8, sf[k]), qf[kk], kk == 0 ? z : s[kb]);
       if (k == NSS / 2) mask_block(0);
       if (k >= NSS / 2)
 #pragma unroll
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
     for (int k = 0; k < NSG; ++k) {
       if (k + PF < NSG) gf[k + PF] = gfrag(Kt, k + PF);
       const int cc = k / NDB, db = k % NDB;
-      dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, gf[k]), dsf[cc], dqa[db], 0, 0, 0);
+      dqa[db] = E::mfma(__builtin_bit_cast(vec8, gf[k]), dsf[cc], dqa[db]);
       if (k == 0) mask_block(1);
       if (k < NSG / 2)
 #pragma unroll
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
     if (j + 1 < n_tiles) step(j + 1, kB, vB, kA, vA);
   }
 
-  if (qrow < N) bwd::store_rows((uint16_t*)a.dq + head + (size_t)qrow * D, dqa, h, a.scale);
+  if (qrow < N) bwd::store_rows<E>((uint16_t*)a.dq + head + (size_t)qrow * D, dqa, h, a.scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -340,12 +341,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
 //                   lane's key on the columns);
 //   gradient phase  dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
 //                   transposed, query steps cc = 0 .. 3.
-// The elementwise P = exp2(c s - LSE log2 e), dS = P (dP - Delta) and the bf16
+// The elementwise P = exp2(c s - LSE log2 e), dS = P (dP - Delta) and the 16-bit
 // packing of block 0 run beside block 1's score MFMAs, those of block 1 beside
 // the gradient MFMAs of block 0's steps; LDS operands are read PF slots ahead.
 // Queries past N (and, under the causal mask, before the key) get weight 0.
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
+  typedef typename E::vec8 vec8;
   constexpr int BQ = 64, RB = D * 2, CPR = D / 8, RPB = 64 / CPR, TILE16 = BQ * CPR;
   constexpr int NLD = TILE16 / 64 / 4, NKB = BQ / 32, NDB = D / 32, NKK = D / 16, NCC = BQ / 16;
   constexpr int NSS = 2 * NKB * NKK;  // score-phase slots
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
   }
 
   // this lane's key: K (signs flipped for a negative scale) and V as MFMA B fragments
-  bf16x8 kreg[NKK], vreg[NKK];
+  vec8 kreg[NKK], vreg[NKK];
   bwd::load_row(kreg, Kg, key, N, D, h, a.flip);
   bwd::load_row(vreg, Vg, key, N, D, h, 0u);
 
@@ -444,7 +446,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
     const bool masked = (CAUSAL && tq * BQ < wave_k0 + 31) || tq * BQ + BQ > N;
     const float c = a.c;
     f32x16 s[NKB], dp[NKB];
-    bf16x8 pf[NCC], dsf[NCC];
+    vec8 pf[NCC], dsf[NCC];
     // element (kb, i) holds query tq*BQ + 4 q4 + (i & 3) of this lane's key,
     // q4 = 8kb + 2h + 4(i >> 3) + ((i >> 2) & 1)
     auto q4_of = [&](int kb, int i) __attribute__((always_inline)) {
@@ -482,8 +484,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
       dp[kb][i] = ds;
       if ((i & 7) == 7) {
         const int cc = 2 * kb + (i >> 3);
-        pf[cc] = bwd::pack8(s[kb], i & 8);
-        dsf[cc] = bwd::pack8(dp[kb], i & 8);
+        pf[cc] = bwd::pack8<E>(s[kb], i & 8);
+        dsf[cc] = bwd::pack8<E>(dp[kb], i & 8);
       }
     };
 
@@ -498,11 +500,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
       const int kb = k / (2 * NKK), kk = (k / 2) % NKK;
       const f32x16 z = {};
       if (k & 1)
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sf[k]), vreg[kk],
-                                                         kk == 0 ? z : dp[kb], 0, 0, 0);
+        dp[kb] = E::mfma(__builtin_bit_cast(vec8, sf[k]), vreg[kk], kk == 0 ? z : dp[kb]);
       else
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sf[k]), kreg[kk],
-                                                        kk == 0 ? z : s[kb], 0, 0, 0);
+        s[kb] = E::mfma(__builtin_bit_cast(vec8, sf[k]), kreg[kk], kk == 0 ? z : s[kb]);
       if (k == NSS / 2) mask_block(0);
       if (k >= NSS / 2)
 #pragma unroll
@@ -515,11 +515,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
       if (k + PF < NSG) gf[k + PF] = gfrag(Qt, Gt, k + PF);
       const int cc = k / (2 * NDB), db = (k / 2) % NDB;
       if (k & 1)
-        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, gf[k]), dsf[cc], dka[db], 0,
-                                                          0, 0);
+        dka[db] = E::mfma(__builtin_bit_cast(vec8, gf[k]), dsf[cc], dka[db]);
       else
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, gf[k]), pf[cc], dva[db], 0,
-                                                          0, 0);
+        dva[db] = E::mfma(__builtin_bit_cast(vec8, gf[k]), pf[cc], dva[db]);
       if (k == 0) mask_block(1);
       if (k < NSG / 2)
 #pragma unroll
@@ -543,8 +541,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
   }
 
   if (key < N) {
-    bwd::store_rows((uint16_t*)a.dk + head + (size_t)key * D, dka, h, a.scale);
-    bwd::store_rows((uint16_t*)a.dv + head + (size_t)key * D, dva, h, 1.0f);
+    bwd::store_rows<E>((uint16_t*)a.dk + head + (size_t)key * D, dka, h, a.scale);
+    bwd::store_rows<E>((uint16_t*)a.dv + head + (size_t)key * D, dva, h, 1.0f);
   }
 }
 

@@ -174,7 +174,7 @@ fa_status check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
   if (st != FA_OK) return st;
   sz.workspace_bytes = 2 * sz.lse_bytes;  // Delta and -LSE log2(e) per row
   if (sizes) *sizes = sz;
-  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
   return check_supported(B, H, N, D);
 }
 

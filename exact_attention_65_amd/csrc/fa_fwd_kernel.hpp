@@ -153,8 +153,9 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 
 // The 16-bit element types of the MFMA kernels: the 8-element operand vector,
 // two fp32 values rounded (to nearest even) into one word, the 32x32x16 MFMA
-// with fp32 accumulation, and the sum of the two elements of a word added to
-// an fp32 accumulator (a dot product with (1, 1)).
+// with fp32 accumulation, the sum of the two elements of a word added to an
+// fp32 accumulator (a dot product with (1, 1)), and the dot product of two
+// words added to an fp32 accumulator.
 struct BF16 {
   typedef bf16x8 vec8;
   __device__ static __forceinline__ uint32_t pack(float lo, float hi) { return pack_bf16(lo, hi); }
@@ -164,6 +165,9 @@ struct BF16 {
   __device__ static __forceinline__ float sum2(uint32_t w, float acc) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+  }
+  __device__ static __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), acc, false);
   }
 };
 struct F16 {
@@ -175,6 +179,9 @@ struct F16 {
   __device__ static __forceinline__ float sum2(uint32_t w, float acc) {
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), ones, acc, false);
+  }
+  __device__ static __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, y), acc, false);
   }
 };
 

@@ -189,7 +189,7 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
  * dout, dq, dk, dv, which share them), lse_bytes that of lse, and
  * workspace_bytes = B*H*N*8 (two floats per query row: sum_d dO O and
  * -LSE log2(e)).  Returns as fa_fwd_query; FA_ERR_UNSUPPORTED also for float32
- * (the backward is bfloat16 only).
+ * (the backward takes bfloat16 and float16) and for D not in {64, 128}.
  */
 fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, fa_dtype dtype,
                        fa_sizes* out);
@@ -209,16 +209,18 @@ fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, f
  * workspace), then one per 128 keys (dk, dv).  No atomics: the result is
  * deterministic.
  *
- * q, k, v, o, dout : [B, H, N, D] bfloat16 contiguous, read only (may alias).
+ * q, k, v, o, dout : [B, H, N, D] contiguous, element type `dtype` (bfloat16
+ *                    or float16), read only (may alias).
  * lse              : float32 [B, H, N] from fa_fwd with the same q, k, v,
  *                    causal and scale.
- * dq, dk, dv       : [B, H, N, D] bfloat16, written; not overlapping any other
+ * dq, dk, dv       : [B, H, N, D] of the same type, written; not overlapping any other
  *                    buffer.
  * workspace        : >= fa_bwd_query's workspace_bytes, 16-byte aligned,
  *                    caller-owned, clobbered.
  *
  * Validation and asynchrony as in fa_fwd; FA_ERR_WORKSPACE when
- * workspace_bytes is too small.  bfloat16, D in {64, 128}.  Allocates nothing.
+ * workspace_bytes is too small.  bfloat16 or float16, D in {64, 128}.
+ * Allocates nothing.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,

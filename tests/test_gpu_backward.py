@@ -147,7 +147,35 @@ def test_backward_outputs_written_and_deterministic():
     assert all(torch.equal(a, b) for a, b in zip(*runs))
 
 
-@pytest.mark.parametrize("w", [fi.BF16_N4096, fi.CAUSAL_SWEEP[3]], ids=lambda w: w.name)
+F16_N = [1, 65, 200, 1000]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", F16_N)
+def test_backward_f16_shapes(N, causal, D):
+    """fp16 inputs and gradients: every element of both heads; the gradients are
+    prefilled with NaN, so every element must be written."""
+    w = fi.Workload(f"bwd_f16_n{N}_d{D}", 970 + F16_N.index(N) * 2 + D // 128, 1, 2, N, D, "f16", causal)
+    gu.log(f"[gpu] backward fp16 N={N} D={D} causal={causal}")
+    q, k, v = gu.workload_tensors(w)
+    o, lse = fa.attention_forward(q, k, v, causal=causal, scale=w.scale)
+    g = [torch.full_like(q, float("nan")) for _ in range(3)]
+    fa.attention_backward(q, k, v, o, lse, _dout(w), causal=causal, scale=w.scale, dq=g[0], dk=g[1], dv=g[2])
+    torch.cuda.synchronize()
+    _compare(w, g, [(0, 0), (0, 1)], w.scale, f"{w.name} causal={causal}")
+
+
+def test_backward_f16_negative_scale():
+    """A negative scale: the sign flip of the register-held Q and K is bit 15,
+    the sign bit of fp16 as of bf16."""
+    w = fi.Workload("bwd_f16_scale_n300_d128", 979, 1, 2, 300, 128, "f16", True)
+    q, k, v = gu.workload_tensors(w)
+    grads = _backward(w, q, k, v, _dout(w), -0.125)
+    _compare(w, grads, [(0, 0), (0, 1)], -0.125, f"{w.name} scale=-0.125")
+
+
+@pytest.mark.parametrize("w", [fi.BF16_N4096, fi.CAUSAL_SWEEP[3], fi.F16_N4096], ids=lambda w: w.name)
 def test_backward_full_size(w):
     """The full-size workloads, in the launch configuration the benchmark
     times; every element of seeded heads."""
