@@ -89,43 +89,96 @@ def read_traffic(workload: str):
         return None
 
 
-def cpu_baseline(w, budget_s: float = 12.0, backward: bool = False):
-    """The fp64 oracle on whole (b, h) heads of the workload until the budget is spent
-    (the gradient oracle with --backward)."""
+def host_info():
+    """CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu": model, "cores_available": len(os.sched_getaffinity(0))}
+
+
+# forward tolerances against the fp64 oracle: max |dO|, mean |dO|, max |dLSE|
+FWD_TOL = {"bf16": (2e-2, 2e-3, 1e-3), "f16": (5e-3, 5e-4, 1e-3), "f32": (1e-5, None, 1e-3)}
+
+
+def cpu_baseline(w, budget_s: float = 12.0, backward: bool = False, gpu_out=None):
+    """The fp64 oracle on whole (b, h) heads of the workload until the budget is
+    spent (the gradient oracle with --backward), on a BLAS pool of
+    min(available cores, 16) threads.  With gpu_out = (O, LSE) as host float
+    arrays, the heads it computes are also compared with the GPU's result."""
     import numpy as np
+    import threadpoolctl
     import fa_inputs as fi
     from oracle import attention_bwd_ref, attention_ref
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        cores = 1
+    cores = min(len(os.sched_getaffinity(0)), 16)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     done = 0
     t_total = 0.0
-    for b, h in heads:
-        q, k, v = fi.head_qkv(w, b, h)
-        do = fi.head_tensor(w, b, h, fi.T_DO) if backward else None
-        if w.dtype == "fp8":
-            import fa_inputs.fp8 as f8
-            from oracle import attention_fp8_ref
-            mx = [f8.head_mx(w, b, h, t) for t in (fi.T_Q, fi.T_K, fi.T_V)]
-        t0 = time.perf_counter()
-        if backward:
-            attention_bwd_ref(q, k, v, do, w.causal, w.scale)
-        elif w.dtype == "fp8":
-            attention_fp8_ref(*mx[0], *mx[1], *mx[2], w.causal, w.scale)
-        else:
-            attention_ref(q, k, v, w.causal, w.scale)
-        t_total += time.perf_counter() - t0
-        done += 1
-        if t_total >= budget_s:
-            break
+    err = {"max_abs_dO": 0.0, "sum_abs_dO": 0.0, "n_O": 0, "max_abs_dLSE": 0.0}
+    with threadpoolctl.threadpool_limits(limits=cores):
+        for b, h in heads:
+            q, k, v = fi.head_qkv(w, b, h)
+            do = fi.head_tensor(w, b, h, fi.T_DO) if backward else None
+            if w.dtype == "fp8":
+                import fa_inputs.fp8 as f8
+                from oracle import attention_fp8_ref
+                mx = [f8.head_mx(w, b, h, t) for t in (fi.T_Q, fi.T_K, fi.T_V)]
+            t0 = time.perf_counter()
+            if backward:
+                attention_bwd_ref(q, k, v, do, w.causal, w.scale)
+                ref = None
+            elif w.dtype == "fp8":
+                ref = attention_fp8_ref(*mx[0], *mx[1], *mx[2], w.causal, w.scale)
+            else:
+                ref = attention_ref(q, k, v, w.causal, w.scale)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if gpu_out is not None and ref is not None:
+                d_o = np.abs(gpu_out[0][b, h].astype(np.float64) - ref[0])
+                d_l = np.abs(gpu_out[1][b, h].astype(np.float64) - ref[1])
+                err["max_abs_dO"] = max(err["max_abs_dO"], float(d_o.max()))
+                err["sum_abs_dO"] += float(d_o.sum())
+                err["n_O"] += d_o.size
+                err["max_abs_dLSE"] = max(err["max_abs_dLSE"], float(d_l.max()))
+            if t_total >= budget_s:
+                break
     flops = w.flops / (w.B * w.H) * done * (BWD_FLOP_FACTOR if backward else 1.0)
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of {len(heads)} (b,h) heads of {w.name}, every query row, numpy float64 "
-                      f"({t_total:.2f} s)"}
+    rec = {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{done} of {len(heads)} (b,h) heads of {w.name}, every query row, numpy float64 "
+                     f"on {cores} BLAS threads ({t_total:.2f} s)"}
+    rec.update(host_info())
+    parity = None
+    if err["n_O"]:
+        parity = {"heads": done, "rows": done * w.nq, "max_abs_dO": err["max_abs_dO"],
+                  "mean_abs_dO": err["sum_abs_dO"] / err["n_O"], "max_abs_dLSE": err["max_abs_dLSE"]}
+        tol = FWD_TOL.get(w.dtype)
+        if tol is not None:
+            parity["tolerance"] = {"max_abs_dO": tol[0], "mean_abs_dO": tol[1], "max_abs_dLSE": tol[2]}
+            parity["pass"] = bool(parity["max_abs_dO"] <= tol[0] and parity["max_abs_dLSE"] <= tol[2]
+                                  and (tol[1] is None or parity["mean_abs_dO"] <= tol[1]))
+    return rec, parity
+
+
+def settle(step, seconds: float) -> int:
+    """Runs steps for about `seconds` before the warm-up.  After an idle spell the
+    chip's launch times first rise by up to a third over some tens of
+    milliseconds of load and then settle (power management); the timed steps are
+    meant to see the settled state.  Returns the number of steps run."""
+    import torch
+    n = 0
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+    return n
 
 
 def naive_context(q, k, v, w, fa_ms, stream, reps: int = 10):
@@ -177,6 +230,10 @@ def main():
     ap.add_argument("--naive-context", action="store_true",
                     help="also time plain torch attention (matmul, softmax, matmul with the N x N scores in "
                          "device memory) on the same inputs, as context only")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of untimed steps before the warm-up, for the clock to settle after idle")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the clock stamps and the MFMA-rate probe")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 times), the known-size "
                          "reference that scales the HBM byte counters")
@@ -193,6 +250,12 @@ def main():
     import torch
     import exact_attention_65_amd as fa
     import fa_inputs as fi
+    from exact_attention_65_amd import probe
+
+    stamps, wall_khz = None, None
+    if not args.no_probe:
+        stamps = torch.zeros((2, probe.STAMP_WORDS), dtype=torch.int64, device="cuda")
+        wall_khz = probe.wallclock_khz()
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
@@ -280,50 +343,52 @@ def main():
             if st != fa.FA_OK:
                 raise fa.FaError(st)
 
+        settle_steps = settle(step, args.settle_s)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
 
-        # timed region: K back-to-back steps, events on the launch stream
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
+        # timed region: K back-to-back steps on the launch stream, an event after
+        # each, so the per-launch durations come from the same launches as the mean;
+        # clock stamps just outside the region give the mean shader clock over it
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        ev0.record(stream)
-        for _ in range(args.steps):
+        if stamps is not None:
+            probe.stamp(stamps[0], sp)
+        evs[0].record(stream)
+        for i in range(args.steps):
             step()
-        ev1.record(stream)
+            evs[i + 1].record(stream)
+        if stamps is not None:
+            probe.stamp(stamps[1], sp)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        region_ms = ev0.elapsed_time(ev1)
+        region_ms = evs[0].elapsed_time(evs[-1])
         ms_per_step = region_ms / args.steps
-
-        # per-launch durations (each launch bracketed by its own events)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for a, b in evs:
-            a.record(stream)
-            step()
-            b.record(stream)
-        torch.cuda.synchronize()
-        launch_ms = np.array([a.elapsed_time(b) for a, b in evs])
-        kernel_ms = float(launch_ms.mean())
+        launch_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+        clock = None
+        if stamps is not None:
+            torch.cuda.synchronize()
+            st_host = stamps.cpu().tolist()
+            clock = round(probe.clock_mhz(st_host[0], st_host[1], wall_khz), 1)
 
         tflops = flops / (ms_per_step * 1e-3) / 1e12
         peak = PEAK_TFLOPS[w.dtype]
-        achieved = flops / (kernel_ms * 1e-3) / 1e12
         elt = {"bf16": 2, "f16": 2, "fp8": 1}.get(w.dtype, 4)
         alg_bytes = w.kv_bytes + w.B * w.H * w.nq * w.D * (elt + 2 if w.dtype == "fp8" else 2 * elt) \
             + 4.0 * w.B * w.H * w.nq + (3.0 * w.B * w.H * w.N * w.D / 32 if w.dtype == "fp8" else 0.0)
         hbm_bound = flops / alg_bytes < peak / PEAK_HBM_GBS * 1e3  # intensity below machine balance
+        # the roofline is taken from the same timed launches as value
         if hbm_bound:
-            roofline = {"bound": "hbm", "achieved": round(alg_bytes / (kernel_ms * 1e-3) / 1e9, 1),
-                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(alg_bytes / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None}
+            gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
         else:
-            roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                        "frac": round(achieved / peak, 4),
+            roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(tflops / peak, 4),
                         "traffic": read_traffic(w.name) if split is None and not args.backward else None}
+        roofline["timing"] = "mean of the timed steps (the same launches as value)"
         rec = {
             "metric": "bwd attention TFLOP/s (10*D per visible (query, key) pair) of workload " + w.name
             if args.backward else METRIC if w.name == HEADLINE else
@@ -350,16 +415,32 @@ def main():
                        "fa_fwd" if split is None else f"fa_fwd_split ({n_ranges} key ranges)",
                        "pct_of_peak": round(100 * tflops / peak, 2),
                        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+                       "launch_ms_median": round(float(np.median(launch_ms)), 5),
+                       "launch_ms_p90": round(float(np.percentile(launch_ms, 90)), 5),
                        "launch_ms_min": round(float(launch_ms.min()), 5),
-                       "launch_ms_median": round(float(np.median(launch_ms)), 5)},
+                       "launch_ms_max": round(float(launch_ms.max()), 5),
+                       "settle_steps": settle_steps,
+                       "shader_clock_mhz": clock},
             "roofline": roofline,
         }
         if args.naive_context and w.dtype in ("bf16", "f16") and not args.backward and split is None:
             rec["context"] = naive_context(q, k, v, w, ms_per_step, stream)
+        if not args.no_probe and not args.sweep:
+            m = probe.mfma_rate(sp)
+            rec["config"]["mfma_probe"] = {
+                "kind": "register-only v_mfma_f32_32x32x16_bf16 loop, 2 waves per SIMD, all CUs",
+                "tflops": round(m["tflops"], 1), "clock_mhz": round(m["clock_mhz"], 1)}
+            if w.dtype in ("bf16", "f16") or args.backward:
+                rec["config"]["pct_of_mfma_probe"] = round(100 * tflops / m["tflops"], 2)
         if not args.no_cpu_baseline and not args.sweep:
+            gpu_out = None
+            if not args.backward and split is None:
+                gpu_out = (o.float().cpu().numpy(), lse.cpu().numpy())
             del q, k, v, o, lse
             torch.cuda.empty_cache()
-            rec["cpu_baseline"] = cpu_baseline(w, backward=args.backward)
+            rec["cpu_baseline"], parity = cpu_baseline(w, backward=args.backward, gpu_out=gpu_out)
+            if parity is not None:
+                rec["parity_vs_oracle"] = parity
         print(json.dumps(rec), flush=True)
 
 

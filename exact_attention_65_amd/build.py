@@ -20,6 +20,10 @@ LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "fa_check.cpp"), os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_bwd.hip"),
            os.path.join(CSRC, "fa_fp8.hip")]
+# measurement probes for the benchmark (clock stamps, MFMA loop): a library of
+# their own, so the attention ABI carries nothing but the attention
+PROBE_LIB_PATH = os.path.join(PKG, "libfa_probe_mi355x.so")
+PROBE_SOURCES = [os.path.join(CSRC, "fa_probe.hip")]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled for all device code.  The kernels'
@@ -38,16 +42,22 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build the library")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library; returns its path.  Always recompiles."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + COMMON + ["-fPIC", "-shared", "-fvisibility=hidden"] + SOURCES + ["-o", tmp]
+def _link(sources, path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
+    cmd = [hipcc()] + COMMON + ["-fPIC", "-shared", "-fvisibility=hidden"] + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the attention library and the probe library; returns the
+    attention library's path.  Always recompiles."""
+    _link(SOURCES, LIB_PATH, verbose)
+    _link(PROBE_SOURCES, PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 

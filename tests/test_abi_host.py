@@ -44,6 +44,35 @@ def test_every_declared_symbol_is_exported():
     assert exported == set(declared_functions())
 
 
+def test_probe_library_exports_what_its_header_declares():
+    if not os.path.exists(fab.PROBE_LIB_PATH):
+        fab.build()
+    text = open(os.path.join(ROOT, "include", "fa_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    declared = set(re.findall(r"^\s*\w+\**\s+\**(fa_probe_\w+)\s*\(", text, flags=re.M))
+    assert declared == {"fa_probe_stamp", "fa_probe_mfma_query", "fa_probe_mfma", "fa_probe_wallclock_khz"}
+    out = subprocess.run(["nm", "-D", "--defined-only", fab.PROBE_LIB_PATH], capture_output=True, text=True).stdout
+    assert set(re.findall(r" T (fa_\w+)$", out, flags=re.M)) == declared
+    from exact_attention_65_amd import probe
+    assert probe.STAMP_BLOCKS == int(re.search(r"#define FA_PROBE_STAMP_BLOCKS (\d+)", text).group(1))
+    lib = probe.lib()
+    blocks, flops = ctypes.c_int(0), ctypes.c_double(0.0)
+    assert lib.fa_probe_mfma_query(0, ctypes.byref(blocks), ctypes.byref(flops)) == -1
+    assert lib.fa_probe_stamp(None, None) == -1
+
+
+def test_probe_clock_from_stamps():
+    from exact_attention_65_amd import probe
+    # XCDs 0..7 in dispatch order, twice; the second stamp 1 ms later at 2000 MHz
+    # (counters per XCD start at different values), constant rate 100 MHz
+    a, b = [], []
+    for blk in range(probe.STAMP_BLOCKS):
+        x = blk % 8
+        a += [10**9 * (x + 1), 5 * 10**6, x]
+        b += [10**9 * (x + 1) + 2 * 10**6, 5 * 10**6 + 10**5, x]
+    assert abs(probe.clock_mhz(a, b, 100000) - 2000.0) < 1e-9
+
+
 def test_version_and_strings():
     assert fa.fa_abi_version() == 5
     for st in range(10):

@@ -39,10 +39,29 @@ def test_traffic_record_is_read_only_for_its_workload():
 
 
 def test_cpu_baseline_record():
-    rec = bench.cpu_baseline(fi.FP32_SMALL, budget_s=0.01)
+    rec, parity = bench.cpu_baseline(fi.FP32_SMALL, budget_s=0.01)
     assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
-    assert rec["value"] > 0 and rec["cores"] >= 1
+    assert rec["value"] > 0 and 1 <= rec["cores"] <= min(16, len(os.sched_getaffinity(0)))
     assert rec["sample"].startswith("1 of 1 (b,h) heads of " + fi.FP32_SMALL.name)
+    assert rec["cores_available"] == len(os.sched_getaffinity(0)) and rec["cpu"]
+    assert parity is None  # no device result to compare
+
+
+def test_cpu_baseline_parity_of_a_given_result():
+    """Handed the oracle's own result (as float32), the parity record passes; a
+    planted error in one output element is reported and fails the bound."""
+    import numpy as np
+    from oracle import attention_ref
+    w = fi.FP32_SMALL
+    q, k, v = fi.head_qkv(w, 0, 0)
+    o, lse = attention_ref(q, k, v, w.causal, w.scale)
+    o32, l32 = o.astype(np.float32)[None, None], lse.astype(np.float32)[None, None]
+    _, par = bench.cpu_baseline(w, budget_s=0.01, gpu_out=(o32, l32))
+    assert par["heads"] == 1 and par["rows"] == w.N and par["pass"]
+    o32 = o32.copy()
+    o32[0, 0, 7, 3] += 1e-3
+    _, par = bench.cpu_baseline(w, budget_s=0.01, gpu_out=(o32, l32))
+    assert not par["pass"] and abs(par["max_abs_dO"] - 1e-3) < 1e-6
 
 
 @pytest.mark.gpu
@@ -60,4 +79,11 @@ def test_bench_line_on_the_gpu():
     rf = d["roofline"]
     assert rf["bound"] in ("mfma", "hbm") and rf["achieved"] > 0 and rf["peak"] > 0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    # value and the roofline come from the same timed launches
+    if rf["bound"] == "mfma":
+        assert abs(rf["achieved"] - d["value"]) <= 0.01
+    c = d["config"]
+    assert c["launch_ms_min"] <= c["launch_ms_median"] <= c["launch_ms_p90"] <= c["launch_ms_max"]
+    assert c["shader_clock_mhz"] is not None and 100 < c["shader_clock_mhz"] < 3000
     assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["cores"] >= 1
+    assert d["parity_vs_oracle"]["pass"] and d["parity_vs_oracle"]["rows"] == fi.FP32_SMALL.N

@@ -61,6 +61,4 @@ def test_f16_full_size_workload():
     gu.log(f"[gpu] workload {w.name}")
     q, k, v = gu.workload_tensors(w)
     o, lse = gu.run(q, k, v, w.causal, w.scale)
-    gu.compare_heads(w, o, lse, fi.sample_heads(w, 2), what=w.name + " full heads")
-    gu.compare_heads(w, o, lse, [(b, h) for b in range(w.B) for h in range(w.H)],
-                     rows_for=lambda h: fi.sample_rows(w, h, 32), what=w.name + " sampled rows")
+    gu.compare_heads(w, o, lse, [(b, h) for b in range(w.B) for h in range(w.H)], what=w.name + " all rows")

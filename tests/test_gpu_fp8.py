@@ -145,11 +145,10 @@ def test_fp8_outputs_written_and_deterministic():
 
 def test_fp8_full_size_workload():
     """The FP8 headline-shape workload in the benchmark's launch configuration:
-    two seeded heads on every row, every head on seeded rows."""
+    every head, every row."""
     w = fi.FP8_N4096
     gu.log(f"[gpu] fp8 workload {w.name}")
     inp = _inputs(w)
     o, lse = _run(inp, w.causal, w.scale)
-    _compare(inp, o, lse, fi.sample_heads(w, 2), w.causal, w.scale, w.name + " full heads")
     _compare(inp, o, lse, [(b, h) for b in range(w.B) for h in range(w.H)], w.causal, w.scale,
-             w.name + " sampled rows", rows_for=lambda h: fi.sample_rows(w, h, 32))
+             w.name + " all rows")

@@ -1,7 +1,8 @@
 """HIP path vs the fp64 oracle on the five workloads at their full sizes, in the
-launch configuration the benchmark times.  Small workloads are compared on
-every element; large ones on seeded samples of heads or rows that the oracle
-computes one by one.
+launch configuration the benchmark times.  The fp32 workload, the bf16 N=4096
+workload and every causal-sweep workload (both variants) are compared on every
+head and every row; the B=32 prefill on 4 seeded (b, h) pairs, every row; the
+N=131072 workload on 256 seeded rows per head plus its first and last rows.
 """
 import numpy as np
 import pytest
@@ -29,25 +30,19 @@ def test_fp32_small_all_elements():
 
 
 def test_bf16_n4096_noncausal():
-    """All 64 heads on 128 seeded rows (+ rows 0 and N-1), and 2 seeded heads on every row."""
+    """All 64 heads, every row."""
     w = fi.BF16_N4096
     o, lse = _run_workload(w)
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    gu.compare_heads(w, o, lse, heads, rows_for=lambda h: fi.sample_rows(w, h, 128), what=w.name + " sampled rows")
-    gu.compare_heads(w, o, lse, fi.sample_heads(w, 2), what=w.name + " full heads")
+    gu.compare_heads(w, o, lse, [(b, h) for b in range(w.B) for h in range(w.H)], what=w.name + " all rows")
 
 
 @pytest.mark.parametrize("variant", [fi.PLAIN, fi.PEAKED])
 @pytest.mark.parametrize("n", fi.CAUSAL_SWEEP_N)
 def test_causal_sweep(n, variant):
+    """All 32 heads, every row."""
     w = fi.CAUSAL_SWEEP[fi.CAUSAL_SWEEP_N.index(n)].with_variant(variant)
     o, lse = _run_workload(w)
-    heads = [(0, h) for h in range(w.H)]
-    if n <= 1024:
-        gu.compare_heads(w, o, lse, heads)
-    else:
-        gu.compare_heads(w, o, lse, heads, rows_for=lambda h: fi.sample_rows(w, h, 64), what=w.name + " sampled rows")
-        gu.compare_heads(w, o, lse, fi.sample_heads(w, 1), what=w.name + " full head")
+    gu.compare_heads(w, o, lse, [(0, h) for h in range(w.H)], what=w.name + " all rows")
 
 
 def test_causal_prefill_b32():
