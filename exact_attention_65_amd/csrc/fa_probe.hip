@@ -20,15 +20,20 @@ constexpr int kProbeThreads = 256;  // 4 waves
 constexpr int kProbeBlocksPerCu = 2;  // two waves per SIMD
 constexpr int kProbeChains = 4;     // independent accumulators per wave
 
-// The shader-clock counter runs per XCD (each XCD has its own), so a stamp is
-// taken on every XCD: kStampBlocks workgroups, dispatched round-robin over the
-// XCDs, each writing {s_memtime, s_memrealtime, XCC id} of its XCD.
+// The shader-clock counter is not one counter shared by the chip: measured,
+// stamps read on different XCDs, and on different compute units of one XCD,
+// are offset from each other.  A stamp is therefore taken on many compute
+// units (kStampBlocks one-wave workgroups, spread over the chip by the
+// dispatcher), each tagged with its XCC id and its shader engine / array /
+// compute-unit ids, and two stamps are compared only where the tags match.
 constexpr int kStampBlocks = FA_PROBE_STAMP_BLOCKS;
 
-__device__ __forceinline__ uint32_t xcc_id() {
-  uint32_t x;
+__device__ __forceinline__ uint32_t cu_tag() {
+  uint32_t x, hw;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
-  return x & 0xF;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+  // HW_ID bits 8-11 CU, 12 shader array, 13-15 shader engine
+  return ((x & 0xF) << 8) | ((hw >> 8) & 0xFF);
 }
 
 __global__ void fa_probe_stamp_kernel(uint64_t* out) {
@@ -38,7 +43,7 @@ __global__ void fa_probe_stamp_kernel(uint64_t* out) {
     uint64_t* o = out + 3 * (size_t)blockIdx.x;
     o[0] = t;
     o[1] = r;
-    o[2] = xcc_id();
+    o[2] = cu_tag();
   }
 }
 

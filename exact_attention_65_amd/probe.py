@@ -44,7 +44,7 @@ def wallclock_khz() -> int:
     return k.value
 
 
-STAMP_BLOCKS = 16  # FA_PROBE_STAMP_BLOCKS
+STAMP_BLOCKS = 2048  # FA_PROBE_STAMP_BLOCKS
 STAMP_WORDS = 3 * STAMP_BLOCKS
 
 
@@ -57,7 +57,7 @@ def stamp(buf, stream) -> None:
 
 def clock_mhz(stamp0, stamp1, wall_khz: int) -> float:
     """Mean shader clock between two stamps (host copies of the stamp buffers),
-    per XCD from that XCD's counter, then the median over the XCDs."""
+    per compute unit from that unit's counter, then the median over the units."""
     def per_xcc(s):
         d = {}
         for b in range(STAMP_BLOCKS):

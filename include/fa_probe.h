@@ -25,14 +25,16 @@
 extern "C" {
 #endif
 
-/* Clock stamp on every XCD: FA_PROBE_STAMP_BLOCKS workgroups, dispatched
- * round-robin over the XCDs, each storing {s_memtime (the 64-bit shader-clock
- * counter of its XCD), s_memrealtime (the 64-bit constant-rate counter), XCC
- * id} at out[3 b .. 3 b + 2].  Two stamps around a region give its mean shader
- * clock on each XCD: d(memtime) / d(realtime) times the constant rate
- * (fa_probe_wallclock_khz), matched by XCC id.  out: 3 x FA_PROBE_STAMP_BLOCKS
+/* Clock stamp on many compute units: FA_PROBE_STAMP_BLOCKS one-wave
+ * workgroups, spread over the chip by the dispatcher, each storing
+ * {s_memtime (the 64-bit shader-clock counter, which differs in offset between
+ * compute units), s_memrealtime (the 64-bit constant-rate counter), a tag of
+ * its compute unit ((XCC id << 8) | HW_ID bits 8-15)} at out[3 b .. 3 b + 2].
+ * Two stamps around a region give its mean shader clock on every compute unit
+ * both reached: d(memtime) / d(realtime) times the constant rate
+ * (fa_probe_wallclock_khz), matched by tag.  out: 3 x FA_PROBE_STAMP_BLOCKS
  * uint64, 8-byte aligned. */
-#define FA_PROBE_STAMP_BLOCKS 16
+#define FA_PROBE_STAMP_BLOCKS 2048
 int fa_probe_stamp(uint64_t* out, fa_stream_t stream);
 
 /* Grid size and bf16 FLOPs of fa_probe_mfma(iters): one workgroup of 4 waves

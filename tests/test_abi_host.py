@@ -63,13 +63,14 @@ def test_probe_library_exports_what_its_header_declares():
 
 def test_probe_clock_from_stamps():
     from exact_attention_65_amd import probe
-    # XCDs 0..7 in dispatch order, twice; the second stamp 1 ms later at 2000 MHz
-    # (counters per XCD start at different values), constant rate 100 MHz
+    # 64 compute-unit tags; the second stamp 1 ms later at 2000 MHz (counters per
+    # unit start at different values, and the second stamp's blocks land on the
+    # units in another order), constant rate 100 MHz
     a, b = [], []
     for blk in range(probe.STAMP_BLOCKS):
-        x = blk % 8
+        x, y = blk % 64, (blk * 7 + 3) % 64
         a += [10**9 * (x + 1), 5 * 10**6, x]
-        b += [10**9 * (x + 1) + 2 * 10**6, 5 * 10**6 + 10**5, x]
+        b += [10**9 * (y + 1) + 2 * 10**6, 5 * 10**6 + 10**5, y]
     assert abs(probe.clock_mhz(a, b, 100000) - 2000.0) < 1e-9
 
 
