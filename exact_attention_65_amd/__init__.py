@@ -38,8 +38,10 @@ FA_ERR_WORKSPACE = 9
 FA_SPLIT_AUTO = 0
 FA_SPLIT_MAX = 256
 
-EXPORTED = ("fa_fwd", "fa_fwd_query", "fa_fwd_split", "fa_fwd_split_query", "fa_bwd", "fa_bwd_query",
-            "fa_fwd_fp8", "fa_fwd_fp8_query", "fa_status_str", "fa_abi_version")
+FA_STATIC_SCRATCH_BYTES = 64 << 20
+
+EXPORTED = ("fa_fwd", "fa_fwd_query", "fa_fwd_split", "fa_fwd_split_query", "fa_fwd_split_static", "fa_bwd",
+            "fa_bwd_query", "fa_fwd_fp8", "fa_fwd_fp8_query", "fa_status_str", "fa_abi_version")
 
 
 class FaSizes(ctypes.Structure):
@@ -69,6 +71,9 @@ def _load():
     lib.fa_fwd_split_query.restype = ctypes.c_int
     lib.fa_fwd_split_query.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.POINTER(FaSizes), ctypes.POINTER(ctypes.c_int)]
+    lib.fa_fwd_split_static.restype = ctypes.c_int
+    lib.fa_fwd_split_static.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                        ctypes.c_int, ctypes.c_int, vp]
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64,
                            ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
@@ -114,6 +119,12 @@ def fa_fwd_split(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, D, c
     """Raw C call: pointers as integers (device addresses), returns the fa_status."""
     return lib().fa_fwd_split(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, D, int(causal),
                               float(scale), int(n_splits), int(dtype), stream)
+
+
+def fa_fwd_split_static(q, k, v, o, lse, B, H, Nq, Nk, D, causal, scale, n_splits, dtype, stream) -> int:
+    """Raw C call: fa_fwd_split with the library's own scratch (no workspace argument)."""
+    return lib().fa_fwd_split_static(q, k, v, o, lse, B, H, Nq, Nk, D, int(causal), float(scale), int(n_splits),
+                                     int(dtype), stream)
 
 
 def fa_fwd_split_query(B, H, Nq, Nk, D, causal, n_splits, dtype):

@@ -17,6 +17,7 @@
 #include <cfloat>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_check.h"
@@ -136,6 +137,35 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* o, float* l
   return a;
 }
 
+// Scratch of fa_fwd_split_static: the key ranges' partial rows live here
+// instead of in a caller workspace.  Each device the library runs on holds its
+// own copy for the life of the process.  In host code `scratch` names a host
+// stand-in, not device memory: kernels get the address hipGetSymbolAddress
+// returns for the current device (scratch_ptr), never the array's name.
+static __device__ __align__(256) unsigned char scratch[FA_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+fa_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FA_OK;
+}
+
 }  // namespace
 
 fa_status device_check() {
@@ -192,4 +222,25 @@ extern "C" __attribute__((visibility("default"))) fa_status fa_fwd_split(
   a.lse_part = a.o_part + (size_t)splits * a.n_bh * a.nq * D;
   if (fa::launch_h16<true>((int)dtype, (int)D, causal != 0, a, s) != hipSuccess) return FA_ERR_HIP;
   return fa::launch_combine((int)dtype, (int)D, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" __attribute__((visibility("default"))) fa_status fa_fwd_split_static(
+    const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Nq,
+    int64_t Nk, int64_t D, int causal, float scale, int n_splits, fa_dtype dtype, fa_stream_t stream) {
+  // host validation first, in fa_fwd_split's order, then the scratch limit
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
+  fa_sizes sz;
+  int splits = 1;
+  fa_status st = fa::check_split_shape(B, H, Nq, Nk, D, causal, n_splits, (int)dtype, &sz, &splits);
+  if (st != FA_OK && st != FA_ERR_UNSUPPORTED) return st;
+  if (!std::isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (st == FA_ERR_UNSUPPORTED) return st;
+  if (sz.workspace_bytes > FA_STATIC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  if ((st = fa::device_check()) != FA_OK) return st;
+  void* ws = nullptr;
+  if (sz.workspace_bytes > 0 && (st = fa::scratch_ptr(&ws)) != FA_OK) return st;
+  // the same kernels as fa_fwd_split; every partial row and log-sum-exp the
+  // merge reads is written by the range kernel first, so nothing is cleared
+  return fa_fwd_split(q, k, v, o, lse, ws, sz.workspace_bytes, B, H, Nq, Nk, D, causal, scale, n_splits, dtype,
+                      stream);
 }

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 /* Identical to hipStream_t.  NULL means the device's null stream. */
 typedef struct ihipStream_t* fa_stream_t;
@@ -181,6 +181,32 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
                        int64_t Nk, int64_t D, int causal, float scale, int n_splits, fa_dtype dtype,
                        fa_stream_t stream);
+
+/* Size of the library's own scratch used by fa_fwd_split_static (64 MiB). */
+#define FA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * fa_fwd_split_static - fa_fwd_split without a caller workspace: for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, results, validation and asynchrony as fa_fwd_split with the same
+ * q, k, v, o, lse, shapes, causal, scale, n_splits, dtype and stream.  The key
+ * ranges' partial results go to a scratch array the library holds per device
+ * (FA_STATIC_SCRATCH_BYTES, held from the first use on a device until the
+ * process ends) instead of a workspace.  Returns FA_ERR_WORKSPACE when the
+ * workspace fa_fwd_split_query reports for these arguments exceeds
+ * FA_STATIC_SCRATCH_BYTES (checked on the host, before any device call).
+ * Allocates nothing: no hipMalloc or hipFree, no allocating library call; the
+ * first call on a device looks up the scratch's device address once.
+ * Every call on one device shares that device's scratch, which keeps the
+ * last call's contents: calls that overlap in time on one device (different
+ * streams, or threads without ordering) race and must be serialised by the
+ * caller.
+ */
+fa_status fa_fwd_split_static(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                              int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
+                              int n_splits, fa_dtype dtype, fa_stream_t stream);
 
 /*
  * fa_bwd_query - buffer sizes of an fa_bwd call.

@@ -75,7 +75,7 @@ def test_probe_clock_from_stamps():
 
 
 def test_version_and_strings():
-    assert fa.fa_abi_version() == 5
+    assert fa.fa_abi_version() == 6
     for st in range(10):
         s = fa.fa_status_str(st)
         assert s.startswith("FA_")
@@ -279,6 +279,32 @@ def test_split_validation_before_any_device_call(kw, expect):
 
 
 # ---------------------------------------------------------------- fa_bwd
+def test_split_static_validation_before_any_device_call():
+    """fa_fwd_split_static checks its arguments and the scratch limit on the host."""
+    p = 1 << 20
+    ok = dict(q=p, k=p, v=p, o=8 * p, lse=16 * p, B=1, H=32, Nq=512, Nk=8192, D=128, causal=1, scale=0.1,
+              n_splits=4, dtype=fa.FA_DTYPE_BF16, stream=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return fa.fa_fwd_split_static(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"],
+                                      a["D"], a["causal"], a["scale"], a["n_splits"], a["dtype"], a["stream"])
+
+    assert call(q=None) == fa.FA_ERR_NULL_POINTER
+    assert call(B=0) == fa.FA_ERR_BAD_SHAPE
+    assert call(Nq=9000) == fa.FA_ERR_BAD_SHAPE  # Nq > Nk under the causal mask
+    assert call(scale=float("nan")) == fa.FA_ERR_BAD_SCALE
+    assert call(dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
+    # 4 ranges x 32 heads x 512 rows x 129 floats = 33.8 MB fits; 8 ranges (67.6 MB) does not
+    st, sz, n = fa.fa_fwd_split_query(1, 32, 512, 8192, 128, 1, 8, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK and n == 8 and sz.workspace_bytes > fa.FA_STATIC_SCRATCH_BYTES
+    assert call(n_splits=8) == fa.FA_ERR_WORKSPACE
+    assert call(B=2) == fa.FA_ERR_WORKSPACE
+    if not gpu_visible():
+        # valid arguments within the limit reach the device check
+        assert call() in (fa.FA_ERR_HIP, fa.FA_ERR_UNSUPPORTED)
+
+
 def test_bwd_query_sizes():
     st, sz = fa.fa_bwd_query(2, 32, 4096, 128, 1, fa.FA_DTYPE_BF16)
     assert st == fa.FA_OK
