@@ -179,6 +179,27 @@ def _dtype_code(dtype) -> int:
     return codes[dtype]
 
 
+def _check_given(t, name: str, shape, dtype, device) -> None:
+    """A caller-supplied output or workspace tensor: the C ABI sees only its
+    address, so its shape, dtype, device and layout are checked here (a tensor
+    that is too small would be written past its end)."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if t.device != device:  # the inputs' device, a GPU (checked before)
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_workspace(t, need: int, device) -> None:
+    import torch
+    _check_given(t, "workspace", None, torch.uint8, device)
+    if t.numel() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes, got {t.numel()}")
+
+
 def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
                       out=None, lse=None, stream=None):
     """O, LSE = attention(q, k, v) for torch tensors [B, H, N, D] on a GPU.
@@ -197,8 +218,10 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    _check_given(out, "out", q.shape, q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_given(lse, "lse", (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -235,10 +258,14 @@ def attention_forward_split(q, k, v, causal: bool = False, scale: float | None =
         raise FaError(st)
     if out is None:
         out = torch.empty_like(q)
+    _check_given(out, "out", q.shape, q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_given(lse, "lse", (B, H, Nq), torch.float32, q.device)
     if workspace is None and sz.workspace_bytes > 0:
         workspace = torch.empty(sz.workspace_bytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check_workspace(workspace, sz.workspace_bytes, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
@@ -269,8 +296,7 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
         if x.dtype != q.dtype or x.shape != q.shape or not x.is_cuda or not x.is_contiguous():
             raise ValueError("q, k, v, o, dout must be contiguous GPU tensors of one shape and dtype")
     B, H, N, D = q.shape
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check_given(lse, "lse", (B, H, N), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     st, sz = fa_bwd_query(B, H, N, D, causal, dt)
@@ -279,8 +305,11 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_given(t, name, q.shape, q.dtype, q.device)
     if workspace is None:
         workspace = torch.empty(sz.workspace_bytes, dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, sz.workspace_bytes, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
@@ -312,8 +341,10 @@ def attention_forward_fp8(q, q_scale, k, k_scale, v, v_scale, causal: bool = Fal
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=q.device)
+    _check_given(out, "out", (B, H, N, D), torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_given(lse, "lse", (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd_fp8(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(), k_scale.data_ptr(), v.data_ptr(),

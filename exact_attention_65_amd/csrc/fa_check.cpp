@@ -281,7 +281,8 @@ __attribute__((visibility("default"))) const char* fa_status_str(fa_status s) {
     case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: every pointer must be 16-byte aligned";
     case FA_ERR_ALIASING: return "FA_ERR_ALIASING: outputs and workspace must not overlap the inputs or each other";
     case FA_ERR_UNSUPPORTED:
-      return "FA_ERR_UNSUPPORTED: needs D in {64,128}, N*D < 2^31, at most 2^31-1 workgroups, a gfx950 device";
+      return "FA_ERR_UNSUPPORTED: a head dimension or dtype the entry point lacks (D in {64,96,128,256} for 16-bit "
+             "forward inputs, {64,128} otherwise), N*D >= 2^31, more than 2^31-1 workgroups, or not a gfx950 device";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call failed";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace_bytes is smaller than the call needs";
   }

@@ -160,7 +160,8 @@ fa_status fa_fwd_split_query(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
  * o = sum_s exp(lse_s - lse) o_s: the online-softmax update of "Flash
  * Attention" (wiki.ai-engineering.at, section "Lösung: Online Softmax")
  * applied to whole ranges.  The pages name this use ("Flash-Decoding", same
- * page, section "Ergebnisse") without giving its steps.
+ * page, section "Flash Attention v2: Noch besser (2023)") without giving its
+ * steps.
  *
  * q, o      : [B, H, Nq, D] bfloat16 or float16 contiguous (o written).
  * k, v      : [B, H, Nk, D] of the same type, contiguous; q, k, v may alias.

@@ -173,6 +173,24 @@ def test_binding_rejects_bad_tensors():
         fa.attention_forward(q, q, q)  # CPU tensors
 
 
+def test_binding_checks_given_outputs():
+    """Caller-supplied outputs and workspaces are checked for shape, dtype,
+    device and layout (the C ABI sees only their addresses)."""
+    import torch
+    dev = torch.device("cpu")
+    good = torch.empty(2, 3, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="dtype"):
+        fa._check_given(good.float(), "out", good.shape, torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="on"):
+        fa._check_given(good, "out", good.shape, torch.bfloat16, torch.device("cuda", 0))
+    with pytest.raises(ValueError, match="contiguous"):
+        fa._check_given(good.transpose(2, 3), "out", None, torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="shape"):
+        fa._check_given(torch.empty(2, 3, 7, 64, dtype=torch.bfloat16), "out", good.shape, torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="bytes"):
+        fa._check_workspace(torch.empty(10, dtype=torch.uint8), 11, dev)
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("source", ["fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip"])
 def test_device_code_has_no_packed_fp32_and_no_spills(source):

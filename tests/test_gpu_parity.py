@@ -163,3 +163,29 @@ def test_status_errors_on_device():
     with pytest.raises(fa.FaError) as e:
         fa.attention_forward(qm, qm, qm, out=o, lse=lse)
     assert e.value.status == fa.FA_ERR_MISALIGNED
+
+
+def test_binding_rejects_bad_output_tensors():
+    """Outputs, gradients and workspaces handed to the torch helpers are checked
+    before any launch: a wrong shape, dtype, device or layout raises ValueError."""
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(1, 2, 64, dtype=torch.float32, device="cuda")
+    bad_outs = [torch.zeros(1, 2, 63, 64, dtype=torch.bfloat16, device="cuda"),   # too small
+                torch.zeros(1, 2, 64, 64, dtype=torch.float16, device="cuda"),    # wrong dtype
+                torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16),                  # host memory
+                torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device="cuda").transpose(2, 3)]
+    for o in bad_outs:
+        with pytest.raises(ValueError):
+            fa.attention_forward(q, q, q, out=o)
+        with pytest.raises(ValueError):
+            fa.attention_forward_split(q, q, q, out=o, n_splits=2)
+    with pytest.raises(ValueError):
+        fa.attention_forward(q, q, q, lse=torch.zeros(1, 2, 63, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.attention_forward_split(q, q, q, n_splits=2,
+                                   workspace=torch.zeros(16, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.attention_backward(q, q, q, q, lse, q, dq=bad_outs[0])
+    with pytest.raises(ValueError):
+        fa.attention_backward(q, q, q, q, lse, q, workspace=torch.zeros(16, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
