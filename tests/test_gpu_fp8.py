@@ -1,15 +1,15 @@
 """fa_fwd_fp8 against the fp64 oracle of the dequantised inputs
 (oracle.attention_fp8_ref).
 
-Tolerance: the bf16 contract (max |dO| <= 2e-2, mean |dO| <= 2e-3, |dLSE| <=
-1e-3), because the roundings left are those of fa_fwd: V is widened to bf16
-exactly and P and O are rounded to bf16.  One more source: the scaled FP8
-matrix instruction does not sum its products at full fp32 precision (measured
-on the device: errors of about 2e-5, at most 1.7e-4, of the sum of the
-products' magnitudes), so score errors grow with the scores; as for fp32
-inputs, the LSE bound is scaled by max(1, max|score| / 5).  The generator's
-inputs dequantise to values of unit scale like the bf16 workloads'; inputs
-with larger values get the O bounds scaled by their RMS.
+Tolerance (tests/error_models.py, fixed before measuring): the bf16 contract
+(max |dO| <= 2e-2, mean |dO| <= 2e-3, |dLSE| <= 1e-3), which covers the
+roundings fa_fwd shares with the bf16 path (V widened to bf16 exactly, P and O
+rounded to bf16), plus the score error of the scaled FP8 matrix instruction,
+whose sums are not specified to fp32 accuracy: under the stated assumption that
+each 64-product sum is accurate to 2^-10 of the sum of its products'
+magnitudes, row i's scores are off by at most E_i, which moves LSE_i by at
+most E_i and O_id by at most 2 E_i max_j |v_jd|.  Both terms are computed per
+row from the inputs; the tests log the largest error / bound ratios.
 """
 import numpy as np
 import pytest
@@ -19,6 +19,7 @@ import exact_attention_65_amd as fa
 import fa_inputs as fi
 import fa_inputs.fp8 as f8
 from oracle import attention_fp8_ref, attention_ref, mx_dequantize
+from tests import error_models as em
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
@@ -42,33 +43,37 @@ def _run(inp, causal, scale, out=None, lse=None):
 
 def _compare(inp, o, lse, heads, causal, scale, what, rows_for=None):
     (q, qs), (k, ks), (v, vs) = inp
-    worst = dict(o_max=0.0, o_mean=0.0, lse_max=0.0, finite=True)
-    n_el, acc = 0, 0.0
-    vrms, sratio = 1.0, 1.0
+    tol = gu.TOL["bf16"]
+    worst = dict(o_ratio=0.0, lse_ratio=0.0, o_max=0.0, lse_max=0.0)
+    mean_err, mean_bound, n_el = 0.0, 0.0, 0
     for b, h in heads:
         rows = None if rows_for is None else rows_for(h)
         o_ref, lse_ref = attention_fp8_ref(q[b, h], qs[b, h], k[b, h], ks[b, h], v[b, h], vs[b, h], causal, scale,
                                            rows=rows)
-        vrms = max(vrms, float(np.sqrt(np.mean(mx_dequantize(v[b, h], vs[b, h]) ** 2))))
-        sratio = max(sratio, gu.score_ratio(mx_dequantize(q[b, h], qs[b, h]), mx_dequantize(k[b, h], ks[b, h]),
-                                            scale, causal))
+        qd, kd, vd = (mx_dequantize(c[b, h], sc[b, h]) for c, sc in ((q, qs), (k, ks), (v, vs)))
+        e_row, o_term = em.fp8_row_terms(qd, kd, vd, causal, scale, rows=rows)
         og = o[b, h].float().cpu().numpy()
         lg = lse[b, h].cpu().numpy()
         if rows is not None:
             og, lg = og[rows], lg[rows]
-        e = gu.errors(og, lg, o_ref, lse_ref)
-        worst["o_max"] = max(worst["o_max"], e["o_max"])
-        worst["lse_max"] = max(worst["lse_max"], e["lse_max"])
-        worst["finite"] &= e["finite"]
-        acc += e["o_mean"] * o_ref.size
-        n_el += o_ref.size
-    worst["o_mean"] = acc / n_el
-    if vrms > 1.0:
-        worst = dict(worst, o_max=worst["o_max"] / vrms, o_mean=worst["o_mean"] / vrms)
-    if sratio > 1.0:
-        worst = dict(worst, lse_max=worst["lse_max"] / sratio)
-    gu.assert_within(worst, "bf16", what + (f" (O errors / V rms {vrms:.1f})" if vrms > 1.0 else "")
-                     + (f" (LSE error / score ratio {sratio:.1f})" if sratio > 1.0 else ""))
+        assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg)), f"{what} (b={b}, h={h}): non-finite output"
+        do = np.abs(og.astype(np.float64) - o_ref)
+        dl = np.abs(lg.astype(np.float64) - lse_ref)
+        worst["o_ratio"] = max(worst["o_ratio"], float((do / (tol["o_max"] + o_term)).max()))
+        worst["lse_ratio"] = max(worst["lse_ratio"], float((dl / (tol["lse"] + e_row)).max()))
+        worst["o_max"] = max(worst["o_max"], float(do.max()))
+        worst["lse_max"] = max(worst["lse_max"], float(dl.max()))
+        mean_err += float(do.sum())
+        mean_bound += float((tol["o_mean"] + o_term).sum())
+        n_el += do.size
+    worst["o_mean_ratio"] = mean_err / mean_bound
+    gu.record(dict(case=what, dtype="fp8", **worst))
+    gu.log(f"  {what}: max|dO|={worst['o_max']:.3e} (err/bound {worst['o_ratio']:.3f}) "
+           f"max|dLSE|={worst['lse_max']:.3e} (err/bound {worst['lse_ratio']:.3f}) "
+           f"mean err/bound {worst['o_mean_ratio']:.3f}")
+    assert worst["o_ratio"] <= 1.0, f"{what}: |dO| above its bound ({worst['o_ratio']:.3f} x)"
+    assert worst["lse_ratio"] <= 1.0, f"{what}: |dLSE| above its bound ({worst['lse_ratio']:.3f} x)"
+    assert worst["o_mean_ratio"] <= 1.0, f"{what}: mean |dO| above its bound ({worst['o_mean_ratio']:.3f} x)"
 
 
 SMALL_N = [1, 17, 64, 65, 128, 129, 200, 333, 1000]
@@ -105,22 +110,24 @@ def test_fp8_block_scales_vary():
     out = [(codes, g.integers(lo, hi, sc.shape).astype(np.uint8)) for (codes, sc), (lo, hi) in zip(inp, ranges)]
     o, lse = _run(out, False, 2.0 ** -7)
     # V values span 2^23 here, so no single absolute bound fits every output;
-    # each element is bounded by the bf16 error model instead: the weights are
-    # normalised by their own rounded sum, so each carries at most 2 * 2^-9
-    # relative error, and O is rounded once more: |dO| <= 2^-8 (W|V|) + 2^-9 |O|
-    # (bounds doubled for margin)
-    (q, qs), (k, ks), (v, vs) = out
+    # each element is bounded by the bf16 error model instead (tests/
+    # error_models.py): the weights are normalised by their own rounded sum, so
+    # each carries at most 2u relative error (u = 2^-8), O is rounded once more
+    # (u |O|), and the FP8 score term adds 2 E_i max_j |v_jd|; times KAPPA
+    u = em.U16["bf16"]
     for hh in range(2):
         qd, kd, vd = (mx_dequantize(c[0, hh], sc[0, hh]) for c, sc in out)
         o_ref, lse_ref = attention_ref(qd, kd, vd, False, 2.0 ** -7)
         wabs, _ = attention_ref(qd, kd, np.abs(vd), False, 2.0 ** -7)
+        e_row, o_term = em.fp8_row_terms(qd, kd, vd, False, 2.0 ** -7)
         err = np.abs(o[0, hh].float().cpu().numpy() - o_ref)
-        bound = 2.0 ** -7 * wabs + 2.0 ** -8 * np.abs(o_ref) + 1e-30
+        bound = em.KAPPA * (2 * u * wabs + u * np.abs(o_ref)) + o_term + 1e-30
         ratio = float((err / bound).max())
-        gu.log(f"  {w.name} head {hh}: max |dO| / bound = {ratio:.3f}, "
-               f"max|dLSE| = {np.abs(lse[0, hh].cpu().numpy() - lse_ref).max():.2e}")
+        dl = np.abs(lse[0, hh].cpu().numpy() - lse_ref)
+        lratio = float((dl / (1e-3 + e_row)).max())
+        gu.log(f"  {w.name} head {hh}: max |dO| / bound = {ratio:.3f}, max |dLSE| / bound = {lratio:.3f}")
         assert ratio <= 1.0, f"{w.name} head {hh}: error above the bf16 error-model bound ({ratio:.3f})"
-        assert np.abs(lse[0, hh].cpu().numpy() - lse_ref).max() <= 1e-3
+        assert lratio <= 1.0, f"{w.name} head {hh}: LSE error above its bound ({lratio:.3f})"
 
 
 def test_fp8_peaked_scores():
