@@ -153,14 +153,19 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 
 // The 16-bit element types of the MFMA kernels: the 8-element operand vector,
 // two fp32 values rounded (to nearest even) into one word, the 32x32x16 MFMA
-// with fp32 accumulation, the sum of the two elements of a word added to an
-// fp32 accumulator (a dot product with (1, 1)), and the dot product of two
+// with fp32 accumulation, the 16x16x32 MFMA and a word holding two ones (for
+// row sums on the matrix core), the sum of the two elements of a word added to
+// an fp32 accumulator (a dot product with (1, 1)), and the dot product of two
 // words added to an fp32 accumulator.
 struct BF16 {
   typedef bf16x8 vec8;
   __device__ static __forceinline__ uint32_t pack(float lo, float hi) { return pack_bf16(lo, hi); }
   __device__ static __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static constexpr uint32_t kOnes2 = 0x3F803F80u;  // two bf16 ones
+  __device__ static __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ float sum2(uint32_t w, float acc) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -175,6 +180,10 @@ struct F16 {
   __device__ static __forceinline__ uint32_t pack(float lo, float hi) { return pack_f16(lo, hi); }
   __device__ static __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static constexpr uint32_t kOnes2 = 0x3C003C00u;  // two fp16 ones
+  __device__ static __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ float sum2(uint32_t w, float acc) {
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
@@ -470,8 +479,9 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   };
 
   // state: o (unnormalised output), m_ref (running reference max, log2 units),
-  // l (sum of the bf16-rounded p: normalises O), lx (sum of fp32 p: LSE),
-  // pf (bf16 P^T of the tile whose values are next), a pending output rescale
+  // l or lsacc (sum of the bf16-rounded p: normalises O), lx (sum of fp32 p:
+  // LSE), pf (bf16 P^T of the tile whose values are next), a pending output
+  // rescale
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -480,6 +490,20 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   f32x16 sA[NKB], sB[NKB];
   vec8 pf[NCC];
   float m_ref = neg_inf(), l = 0.0f, lx = 0.0f, mu = 0.0f;
+  // The sum of the rounded P is taken on the matrix core for D <= 128: one
+  // 16x16x32 MFMA per value step multiplies a constant 0/1 operand with that
+  // step's P^T fragment (the B operand of the value MFMAs, read again as the B
+  // operand of the 16x16x32 form: lane L holds query L % 32, keys 8 (L / 32)
+  // .. +7 of the step, and lands in column L % 16, k block L / 16).  Row 0 of
+  // the constant picks k blocks 0 and 2 (lanes 0 and 32: both key halves of
+  // query n), row 1 blocks 1 and 3 (lanes 17 and 49: query n + 16), so lane
+  // n < 16 accumulates query n in lsacc[0] and query n + 16 in lsacc[1].  This
+  // replaces 8 dot products per step on the vector unit.  D = 256 has no
+  // registers left for it and keeps the dot products (into l).
+  constexpr bool kMfmaSum = D <= 128;
+  f32x4 lsacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const uint32_t one2 = (lane == 0 || lane == 32 || lane == 17 || lane == 49) ? E::kOnes2 : 0u;
+  const vec8 ones_op = __builtin_bit_cast(vec8, u32x4{one2, one2, one2, one2});
   // raw tile maxima above thr move the reference: c thr = m_ref + kTau (-inf
   // until a key is seen; +inf when that overflows, at the smallest c, where
   // every c s is too small to move it)
@@ -529,7 +553,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
       if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
         const float m_new = vmax(m_ref, mx * c);
         const float alpha = m_new == neg_inf() ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-        l *= alpha;
+        if constexpr (!kMfmaSum) l *= alpha;
         lx *= alpha;
         m_ref = m_new;
         pend = true;
@@ -539,7 +563,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
       }
       pin(mu);
       pin(pend_alpha);
-      pin(l);
+      if constexpr (!kMfmaSum) pin(l);
       pin(lx);
       pin(thr);
     }
@@ -555,8 +579,10 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
     // miscompiles __builtin_bit_cast applied to an element of a vector variable
     const uint32_t w0 = E::pack(s[kb][base + 0], s[kb][base + 1]);
     const uint32_t w1 = E::pack(s[kb][base + 2], s[kb][base + 3]);
-    lsum[half] = E::sum2(w0, lsum[half]);
-    lsum[half] = E::sum2(w1, lsum[half]);
+    if constexpr (!kMfmaSum) {
+      lsum[half] = E::sum2(w0, lsum[half]);
+      lsum[half] = E::sum2(w1, lsum[half]);
+    }
     // the first slice of a phase starts the fp32 sum (adding it to a zero
     // would cost an instruction: x + 0 is not x for x = -0)
     const float part = (s[kb][base + 0] + s[kb][base + 1]) + (s[kb][base + 2] + s[kb][base + 3]);
@@ -564,7 +590,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
     uint32_t r0 = w0, r1 = w1;
     pin(r0);
     pin(r1);
-    pin(lsum[half]);
+    if constexpr (!kMfmaSum) pin(lsum[half]);
     pin(xsum[half]);
     return u32x2{r0, r1};
   };
@@ -585,7 +611,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
     // over the other wave on the SIMD, which is then typically in its
     // MFMA-heavy phase B
     __builtin_amdgcn_s_setprio(1);
-    lsum[0] = lsum[1] = 0.0f;
+    if constexpr (!kMfmaSum) lsum[0] = lsum[1] = 0.0f;
     u32x4 kf[RKA];
 #pragma unroll
     for (int k = 0; k < PFA; ++k) kf[k % RKA] = kfrag(Kt, k);
@@ -608,7 +634,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
       const u32x4 x = {pw[2 * cc][0], pw[2 * cc][1], pw[2 * cc + 1][0], pw[2 * cc + 1][1]};
       pf[cc] = __builtin_bit_cast(vec8, x);
     }
-    l += lsum[0] + lsum[1];
+    if constexpr (!kMfmaSum) l += lsum[0] + lsum[1];
     lx += xsum[0] + xsum[1];
     __builtin_amdgcn_s_setprio(0);
   };
@@ -624,11 +650,20 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
       if (k <= NKB) ref_slice(sn, k);
       const int db = k % NDB, cc = k / NDB;
       o[db] = E::mfma(__builtin_bit_cast(vec8, vf[k % RVB]), pf[cc], o[db]);
+      if constexpr (kMfmaSum)
+        if (db == NDB - 1) lsacc = E::mfma16(ones_op, pf[cc], lsacc);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto apply_rescale = [&]() __attribute__((always_inline)) {
     if (pend) {
+      if constexpr (kMfmaSum) {
+        // lsacc[1] of lane n < 16 belongs to query n + 16 (lane n + 16)
+        const float a_hi = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(((lane + 16) & 63) << 2, __builtin_bit_cast(int, pend_alpha)));
+        lsacc[0] *= pend_alpha;
+        lsacc[1] *= a_hi;
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -692,7 +727,20 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
 
   // epilogue: O = o / l, LSE = (m + log2 lx) ln 2.  A split row that sees no
   // key of its range (l = 0) records LSE = -inf and O = 0.
-  const float l_tot = pair_sum(l);
+  float l_tot;
+  if constexpr (kMfmaSum) {
+    // query c32's sum sits in lane c32 % 16, element c32 / 16 (each element
+    // is copied to a scalar before its bit cast: see the packed words above)
+    float e0 = lsacc[0], e1 = lsacc[1];
+    pin(e0);
+    pin(e1);
+    const int src = (c32 & 15) << 2;
+    const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, e0)));
+    const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, e1)));
+    l_tot = c32 < 16 ? s0 : s1;
+  } else {
+    l_tot = pair_sum(l);
+  }
   const float lx_tot = pair_sum(lx);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (qrow < NQ) {
