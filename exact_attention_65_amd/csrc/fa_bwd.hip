@@ -3,7 +3,10 @@
 // Two launches on the caller's stream: fa_bwd_dq_kernel (one workgroup per 128
 // query rows: dq, and per row Delta = rowsum(dO O) and -LSE log2(e) into the
 // workspace), then fa_bwd_dkdv_kernel (one workgroup per 128 keys: dk, dv),
-// which reads both.
+// which reads both.  When the dq and dk/dv workgroups together fit one per
+// compute unit, the two walks over the tiles can run side by side instead:
+// fa_bwd_delta_kernel writes Delta and -LSE log2(e), then fa_bwd_fused_kernel
+// runs the dk/dv and dq workgroups in one grid.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -18,15 +21,32 @@ namespace fa {
 namespace {
 
 template <typename Kern>
-hipError_t launch(Kern kern, const BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(kern, dim3(a.n_blocks), dim3(kBwdThreads), 0, s, a);
+hipError_t launch(Kern kern, const BwdArgs& a, hipStream_t s, int mult = 1) {
+  hipLaunchKernelGGL(kern, dim3(a.n_blocks * mult), dim3(kBwdThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// true when the dq and dk/dv grids together hold at most one workgroup per
+// compute unit of the current device
+bool fuse_bwd(const BwdArgs& a) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  return 2LL * a.n_blocks <= cus;
+}
+
+template <typename E, int D>
+hipError_t launch_fused(bool causal, const BwdArgs& a, hipStream_t s) {
+  hipError_t e = launch(fa_bwd_delta_kernel<E, D>, a, s);
+  if (e != hipSuccess) return e;
+  return causal ? launch(fa_bwd_fused_kernel<E, D, true>, a, s, 2) : launch(fa_bwd_fused_kernel<E, D, false>, a, s, 2);
 }
 
 template <typename E>
 hipError_t launch_bwd_typed(int D, bool causal, BwdArgs a, float scale, hipStream_t s) {
   // dq kernel: Q's signs carry the sign of scale (the sign bit of both 16-bit types is bit 15)
   a.flip = std::signbit(scale) && scale != 0.0f ? 0x80008000u : 0u;
+  if (fuse_bwd(a)) return D == 128 ? launch_fused<E, 128>(causal, a, s) : launch_fused<E, 64>(causal, a, s);
   hipError_t e;
   if (D == 128) e = causal ? launch(fa_bwd_dq_kernel<E, 128, true>, a, s) : launch(fa_bwd_dq_kernel<E, 128, false>, a, s);
   else e = causal ? launch(fa_bwd_dq_kernel<E, 64, true>, a, s) : launch(fa_bwd_dq_kernel<E, 64, false>, a, s);

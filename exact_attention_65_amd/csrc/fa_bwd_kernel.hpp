@@ -148,7 +148,52 @@ __device__ __forceinline__ void store_rows(uint16_t* out_row, const f32x16 (&acc
     }
 }
 
+// Delta = sum_d dO O of this lane's row (rows past N: 0): dot products of the
+// 16-bit pairs of its half of the row (dO already in dof), then the two
+// halves' sum.
+template <typename E, int D>
+__device__ __forceinline__ float row_delta(const typename E::vec8 (&dof)[D / 16], const uint16_t* Og, int row,
+                                           int N, int h) {
+  constexpr int NKK = D / 16;
+  typename E::vec8 of[NKK];
+  load_row(of, Og, row, N, D, h, 0u);
+  float dsum = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const u32x4 x = __builtin_bit_cast(u32x4, dof[kk]), y = __builtin_bit_cast(u32x4, of[kk]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t xe = x[e], ye = y[e];
+      dsum = E::dot2(xe, ye, dsum);
+    }
+  }
+  return pair_sum(dsum);
+}
+
 }  // namespace bwd
+
+// ---------------------------------------------------------------------------
+// Delta and -LSE log2(e) of every row into the workspace, by the dq kernel's
+// prologue arithmetic (4 waves x 32 rows per workgroup): the first launch of a
+// backward whose dq and dk/dv workgroups share the second.
+template <typename E, int D>
+__global__ __launch_bounds__(kBwdThreads) void fa_bwd_delta_kernel(BwdArgs a) {
+  typedef typename E::vec8 vec8;
+  constexpr int NKK = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, c32 = lane & 31;
+  const int N = a.n;
+  const int bh = blockIdx.x / a.n_blk, qb = blockIdx.x % a.n_blk;
+  const int qrow = qb * kBwdRows + wave * 32 + c32;
+  const size_t head = (size_t)bh * N * D;
+  vec8 dof[NKK];
+  bwd::load_row(dof, (const uint16_t*)a.dout + head, qrow, N, D, h, 0u);
+  const float delta = bwd::row_delta<E, D>(dof, (const uint16_t*)a.o + head, qrow, N, h);
+  if (qrow < N && h == 0) {
+    a.delta[(size_t)bh * N + qrow] = delta;
+    a.nlse2[(size_t)bh * N + qrow] = -(a.lse[(size_t)bh * N + qrow] * kLog2e);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // dQ (and Delta): 4 waves x 32 query rows; 64-key K and V tiles streamed
@@ -157,8 +202,13 @@ __device__ __forceinline__ void store_rows(uint16_t* out_row, const f32x16 (&acc
 // the columns: the forward's orientation), 16 MFMAs dP^T = V dO^T, the
 // elementwise dS^T = P^T (dP^T - Delta), and 16 MFMAs dQ^T += K^T dS^T with
 // K^T read transposed from the same tile (for D = 128; half as many for 64).
-template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
+//
+// The body takes the workgroup index blk (blockIdx.x of its own launch, or its
+// offset in a launch shared with the dk/dv workgroups).  DELTA: the prologue
+// also writes Delta and -LSE log2(e) of the rows to the workspace (otherwise
+// fa_bwd_delta_kernel has written them).
+template <typename E, int D, bool CAUSAL, bool DELTA>
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
   typedef typename E::vec8 vec8;
   constexpr int BN = 64, RB = D * 2, CPR = D / 8, RPB = 64 / CPR, TILE16 = BN * CPR;
   constexpr int NLD = TILE16 / 64 / 4, NKB = BN / 32, NDB = D / 32, NKK = D / 16, NCC = BN / 16;
@@ -168,7 +218,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
   const int N = a.n;
-  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL, true);
+  const HeadItem wi = head_item(xcd_remap(blk, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL, true);
   const int bh = wi.bh;
   const int qb = CAUSAL ? a.n_blk - 1 - wi.idx : wi.idx;  // causal: longest query blocks first
   const int q0 = qb * kBwdRows;
@@ -195,23 +245,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   vec8 qf[NKK], dof[NKK];
   bwd::load_row(qf, Qg, qrow, N, D, h, a.flip);
   bwd::load_row(dof, dOg, qrow, N, D, h, 0u);
-  float dsum = 0.0f;
-  {
-    vec8 of[NKK];
-    bwd::load_row(of, Og, qrow, N, D, h, 0u);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const u32x4 x = __builtin_bit_cast(u32x4, dof[kk]), y = __builtin_bit_cast(u32x4, of[kk]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t xe = x[e], ye = y[e];
-        dsum = E::dot2(xe, ye, dsum);
-      }
-    }
-  }
-  const float delta = pair_sum(dsum);
+  const float delta = bwd::row_delta<E, D>(dof, Og, qrow, N, h);
   const float lse2 = qrow < N ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.0f;
-  if (qrow < N && h == 0) {
+  if (DELTA && qrow < N && h == 0) {
     a.delta[(size_t)bh * N + qrow] = delta;
     a.nlse2[(size_t)bh * N + qrow] = -lse2;
   }
@@ -331,6 +367,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   if (qrow < N) bwd::store_rows<E>((uint16_t*)a.dq + head + (size_t)qrow * D, dqa, h, a.scale);
 }
 
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
+  bwd_dq_body<E, D, CAUSAL, true>(a, blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // dK and dV: 4 waves x 32 keys; 64-query Q and dO tiles streamed through
 // double-buffered LDS, with the rows' -LSE log2(e) and Delta.  Per tile and
@@ -346,7 +387,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
 // the gradient MFMAs of block 0's steps; LDS operands are read PF slots ahead.
 // Queries past N (and, under the causal mask, before the key) get weight 0.
 template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
   typedef typename E::vec8 vec8;
   constexpr int BQ = 64, RB = D * 2, CPR = D / 8, RPB = 64 / CPR, TILE16 = BQ * CPR;
   constexpr int NLD = TILE16 / 64 / 4, NKB = BQ / 32, NDB = D / 32, NKK = D / 16, NCC = BQ / 16;
@@ -363,7 +404,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
   const int N = a.n;
-  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL, false);
+  const HeadItem wi = head_item(xcd_remap(blk, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL, false);
   const int bh = wi.bh;
   const int kblk = wi.idx;  // causal: the first key blocks see the most queries
   const int k0 = kblk * kBwdRows;
@@ -544,6 +585,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
     bwd::store_rows<E>((uint16_t*)a.dk + head + (size_t)key * D, dka, h, a.scale);
     bwd::store_rows<E>((uint16_t*)a.dv + head + (size_t)key * D, dva, h, 1.0f);
   }
+}
+
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
+  bwd_dkdv_body<E, D, CAUSAL>(a, blockIdx.x);
+}
+
+// ---------------------------------------------------------------------------
+// dk/dv and dq workgroups in one launch (the first n_blocks workgroups are
+// dk/dv ones, the next n_blocks dq ones), after fa_bwd_delta_kernel: for grids
+// that leave most compute units idle, where each kernel's time is the walk of
+// its longest workgroup over the tiles and the two walks can run side by side
+// instead of one after the other.  The two are independent given Delta and
+// -LSE log2(e).  One workgroup per CU (the dk/dv body's registers, both
+// bodies' LDS).
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_fused_kernel(BwdArgs a) {
+  if ((int)blockIdx.x < a.n_blocks) bwd_dkdv_body<E, D, CAUSAL>(a, blockIdx.x);
+  else bwd_dq_body<E, D, CAUSAL, false>(a, (int)blockIdx.x - a.n_blocks);
 }
 
 }  // namespace fa

@@ -89,6 +89,25 @@ def test_backward_small_shapes(N, causal, D):
     _compare(w, grads, [(0, 0), (0, 1)], w.scale, f"{w.name} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_fused_and_separate_launches(causal):
+    """The same heads through both launch plans: B=1, H=32, N=512 gives 128 dq
+    and 128 dk/dv workgroups, one per compute unit of the 256, so fa_bwd runs
+    them in one launch after the Delta kernel; H=33 gives 264 and the two
+    kernels run one after the other.  The inputs of a head depend only on its
+    (b, h) and the seed, so heads 0 and 1 are the same in both."""
+    results = {}
+    for H in (32, 33):
+        w = fi.Workload("bwd_plans_n512_d128", 770, 1, H, 512, 128, "bf16", causal)
+        gu.log(f"[gpu] backward N=512 H={H} causal={causal}")
+        q, k, v = gu.workload_tensors(w)
+        grads = _backward(w, q, k, v, _dout(w), w.scale)
+        _compare(w, grads, [(0, 0), (0, 1), (0, H - 1)], w.scale, f"{w.name} H={H} causal={causal}")
+        results[H] = [g[:, :2].float().cpu() for g in grads]
+    diff = max(float((a - b).abs().max()) for a, b in zip(results[32], results[33]))
+    gu.log(f"  largest difference between the two plans on heads 0-1: {diff:.3e}")
+
+
 @pytest.mark.parametrize("scale", [-0.125, 0.3, 1e-3])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_other_scales(scale, causal):
