@@ -210,9 +210,9 @@ def test_every_kernel_stub_is_defined():
     assert undefined == []
     kernels = set(re.findall(r"(_ZN2fa\d+fa_\w+_kernelI\w+)", out))
     # bf16 and fp16: D (64, 96, 128, 256) x causal x split; fp32: D x causal; merge: D x (bf16, fp16);
-    # backward: (bf16, fp16) x 2 kernels x D x causal; fp8: D x causal; one-query-row: (bf16, fp16) x D
-    # (64, 128, 256)
-    assert len(kernels) == 32 + 4 + 8 + 16 + 4 + 6, kernels
+    # backward: (bf16, fp16) x 3 kernels (dq, dk/dv, both in one grid) x D x causal and the Delta kernel
+    # (bf16, fp16) x D; fp8: D x causal; one-query-row: (bf16, fp16) x D (64, 128, 256)
+    assert len(kernels) == 32 + 4 + 8 + 24 + 4 + 4 + 6, kernels
 
 
 # ---------------------------------------------------------------- fa_fwd_split

@@ -74,13 +74,17 @@ def test_every_tile_barrier_drains_vmcnt(asm):
 
 def test_backward_kernels_present(bwd_asm):
     names = [n for n, _ in _kernels(bwd_asm)]
-    # (bf16, fp16) x D (64, 128) x causal for each of the two kernels
+    # (bf16, fp16) x D (64, 128) x causal for each of the three tile kernels (dq, dk/dv, both in one
+    # grid), and (bf16, fp16) x D for the Delta kernel
     assert sum("bwd_dq" in n for n in names) == 8, names
     assert sum("bwd_dkdv" in n for n in names) == 8, names
+    assert sum("bwd_fused" in n for n in names) == 8, names
+    assert sum("bwd_delta" in n for n in names) == 4, names
 
 
 def test_backward_tile_barriers_drain_vmcnt(bwd_asm):
-    for name, body in _kernels(bwd_asm):
+    # every backward kernel but the Delta one streams tiles through LDS
+    for name, body in [(n, b) for n, b in _kernels(bwd_asm) if "bwd_delta" not in n]:
         waits = _barrier_waits(body)
         assert waits, f"{name}: no barrier after a tile load"
         bad = [i for i, ok in waits if not ok]
