@@ -42,19 +42,22 @@ hipError_t launch_fused(bool causal, const BwdArgs& a, hipStream_t s) {
   return causal ? launch(fa_bwd_fused_kernel<E, D, true>, a, s, 2) : launch(fa_bwd_fused_kernel<E, D, false>, a, s, 2);
 }
 
+template <typename E, int D>
+hipError_t launch_bwd_d(bool causal, const BwdArgs& a, hipStream_t s) {
+  if (fuse_bwd(a)) return launch_fused<E, D>(causal, a, s);
+  const hipError_t e = causal ? launch(fa_bwd_dq_kernel<E, D, true>, a, s) : launch(fa_bwd_dq_kernel<E, D, false>, a, s);
+  if (e != hipSuccess) return e;
+  return causal ? launch(fa_bwd_dkdv_kernel<E, D, true>, a, s) : launch(fa_bwd_dkdv_kernel<E, D, false>, a, s);
+}
+
 template <typename E>
 hipError_t launch_bwd_typed(int D, bool causal, BwdArgs a, float scale, hipStream_t s) {
-  // dq kernel: Q's signs carry the sign of scale (the sign bit of both 16-bit types is bit 15)
+  // Q's signs (dq work) and K's (dk/dv work) carry the sign of scale (the sign
+  // bit of both 16-bit types is bit 15)
   a.flip = std::signbit(scale) && scale != 0.0f ? 0x80008000u : 0u;
-  if (fuse_bwd(a)) return D == 128 ? launch_fused<E, 128>(causal, a, s) : launch_fused<E, 64>(causal, a, s);
-  hipError_t e;
-  if (D == 128) e = causal ? launch(fa_bwd_dq_kernel<E, 128, true>, a, s) : launch(fa_bwd_dq_kernel<E, 128, false>, a, s);
-  else e = causal ? launch(fa_bwd_dq_kernel<E, 64, true>, a, s) : launch(fa_bwd_dq_kernel<E, 64, false>, a, s);
-  if (e != hipSuccess) return e;
-  // dkdv kernel: K's signs carry it
-  if (D == 128)
-    return causal ? launch(fa_bwd_dkdv_kernel<E, 128, true>, a, s) : launch(fa_bwd_dkdv_kernel<E, 128, false>, a, s);
-  return causal ? launch(fa_bwd_dkdv_kernel<E, 64, true>, a, s) : launch(fa_bwd_dkdv_kernel<E, 64, false>, a, s);
+  if (D == 128) return launch_bwd_d<E, 128>(causal, a, s);
+  if (D == 96) return launch_bwd_d<E, 96>(causal, a, s);
+  return launch_bwd_d<E, 64>(causal, a, s);
 }
 
 hipError_t launch_bwd(int dtype, int D, bool causal, const BwdArgs& a, float scale, hipStream_t s) {

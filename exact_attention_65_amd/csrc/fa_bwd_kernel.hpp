@@ -210,7 +210,10 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_delta_kernel(BwdArgs a) {
 template <typename E, int D, bool CAUSAL, bool DELTA>
 __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
   typedef typename E::vec8 vec8;
-  constexpr int BN = 64, RB = D * 2, CPR = D / 8, RPB = 64 / CPR, TILE16 = BN * CPR;
+  // D = 96 rows sit in LDS as 128-wide rows whose last 4 chunks stay zero (the
+  // LDS addresses are the D = 128 ones); global rows keep their width
+  constexpr int DP = D == 96 ? 128 : D;
+  constexpr int BN = 64, RB = DP * 2, GRB = D * 2, CPR = DP / 8, RPB = 64 / CPR, TILE16 = BN * CPR;
   constexpr int NLD = TILE16 / 64 / 4, NKB = BN / 32, NDB = D / 32, NKK = D / 16, NCC = BN / 16;
   __shared__ u32x4 kA[TILE16], kB[TILE16], vA[TILE16], vB[TILE16];
 
@@ -252,17 +255,23 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
     a.nlse2[(size_t)bh * N + qrow] = -lse2;
   }
 
+  // LDS position cl of a row holds global chunk cl ^ swizzle(row); at D = 96
+  // the lanes whose chunk is past the row load nothing
   uint32_t koff[NLD];
+  bool kon[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int row = (wave * NLD + i) * RPB + lane / CPR;
-    koff[i] = row * RB + (((lane % CPR) ^ bwd::bswz<D>(row)) * 16);
+    const int kg = (lane % CPR) ^ bwd::bswz<DP>(row);
+    koff[i] = row * GRB + kg * 16;
+    kon[i] = kg < D / 8;
   }
   auto issue = [&](u32x4* dst, const uint16_t* src, int kv0) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(N - kv0) * RB), kRsrcWord3);
+        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(N - kv0) * GRB), kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) lds_load16(r, dst + (wave * NLD + i) * 64, koff[i]);
+    for (int i = 0; i < NLD; ++i)
+      if (D == DP || kon[i]) lds_load16(r, dst + (wave * NLD + i) * 64, koff[i]);
   };
 
   f32x16 dqa[NDB];
@@ -274,12 +283,12 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
   // operand of score slot f: rows of block f / (2 NKK), chunk (f / 2) % NKK of
   // K (even f: S^T) or V (odd f: dP^T); of dQ slot f: key step f / NDB, d
   // block f % NDB of K^T
-  const uint32_t rbase = bwd::row_base<D>(c32, h), tb0 = bwd::tr_base<D>(lane, 0), tb1 = bwd::tr_base<D>(lane, 1);
+  const uint32_t rbase = bwd::row_base<DP>(c32, h), tb0 = bwd::tr_base<DP>(lane, 0), tb1 = bwd::tr_base<DP>(lane, 1);
   auto sfrag = [&](const u32x4* Kt, const u32x4* Vt, int f) __attribute__((always_inline)) {
-    return bwd::row_frag<D>((f & 1) ? Vt : Kt, rbase, f / (2 * NKK), (f / 2) % NKK);
+    return bwd::row_frag<DP>((f & 1) ? Vt : Kt, rbase, f / (2 * NKK), (f / 2) % NKK);
   };
   auto gfrag = [&](const u32x4* Kt, int f) __attribute__((always_inline)) {
-    return bwd::tr_frag<D>(Kt, tb0, tb1, f % NDB, f / NDB);
+    return bwd::tr_frag<DP>(Kt, tb0, tb1, f % NDB, f / NDB);
   };
   // per tile and wave, two phases of MFMA slots: the score phase (S^T and
   // dP^T, block kb = 0 then 1), then the dQ phase (key steps cc = 0 .. 3);
@@ -287,8 +296,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
   // beside the dQ MFMAs of block 0's steps; LDS operands are read PF slots ahead
   auto compute = [&](const u32x4* Kt, const u32x4* Vt, int j) __attribute__((always_inline)) {
     constexpr int NSS = 2 * NKB * NKK, NSG = NDB * NCC, PF = 4;
-    constexpr int EPS = 16 / (NSS / 2), EPG = 16 / (NSG / 2);
-    static_assert(EPS * (NSS / 2) == 16 && EPG * (NSG / 2) == 16 && NKB == 2, "slot layout");
+    // a block's 16 elementwise steps spread over half a phase's slots: slot
+    // k of that half takes steps [16k / H, 16(k+1) / H), H = slots / 2
+    constexpr int HS = NSS / 2, HG = NSG / 2;
+    static_assert(HS <= 16 && HG <= 16 && NKB == 2, "slot layout");
     const int kv0 = j * BN;
     const bool masked = kv0 + BN > N || (CAUSAL && kv0 + BN - 1 > wave_q0);
     f32x16 s[NKB], dp[NKB];
@@ -327,7 +338,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
       if (k == NSS / 2) mask_block(0);
       if (k >= NSS / 2)
 #pragma unroll
-        for (int e = 0; e < EPS; ++e) ds_elem(0, (k - NSS / 2) * EPS + e);
+        for (int e = (k - HS) * 16 / HS; e < (k - HS + 1) * 16 / HS; ++e) ds_elem(0, e);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -338,7 +349,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
       if (k == 0) mask_block(1);
       if (k < NSG / 2)
 #pragma unroll
-        for (int e = 0; e < EPG; ++e) ds_elem(1, k * EPG + e);
+        for (int e = k * 16 / HG; e < (k + 1) * 16 / HG; ++e) ds_elem(1, e);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -389,14 +400,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
 template <typename E, int D, bool CAUSAL>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
   typedef typename E::vec8 vec8;
-  constexpr int BQ = 64, RB = D * 2, CPR = D / 8, RPB = 64 / CPR, TILE16 = BQ * CPR;
+  constexpr int DP = D == 96 ? 128 : D;  // LDS row width (as in the dq body)
+  constexpr int BQ = 64, RB = DP * 2, GRB = D * 2, CPR = DP / 8, RPB = 64 / CPR, TILE16 = BQ * CPR;
   constexpr int NLD = TILE16 / 64 / 4, NKB = BQ / 32, NDB = D / 32, NKK = D / 16, NCC = BQ / 16;
   constexpr int NSS = 2 * NKB * NKK;  // score-phase slots
   constexpr int NSG = 2 * NDB * NCC;  // gradient-phase slots
   constexpr int PF = 4;               // operand reads in flight
-  constexpr int EPS = 16 / (NSS / 2); // softmax elements per slot (block 0 beside block 1's MFMAs)
-  constexpr int EPG = 16 / (NSG / 2); // softmax elements per slot (block 1 beside the gradient MFMAs)
-  static_assert(EPS * (NSS / 2) == 16 && EPG * (NSG / 2) == 16 && NKB == 2, "slot layout");
+  // softmax steps of a block per slot: slot k of the half phase beside which a
+  // block's 16 steps run takes steps [16k / H, 16(k+1) / H) (block 0 beside
+  // block 1's score MFMAs, block 1 beside the gradient MFMAs)
+  constexpr int HS = NSS / 2, HG = NSG / 2;
+  static_assert(HS <= 16 && HG <= 16 && NKB == 2, "slot layout");
   __shared__ u32x4 qA[TILE16], qB[TILE16], gA[TILE16], gB[TILE16];
   __shared__ f32x4 lA[BQ / 4], lB[BQ / 4], dA[BQ / 4], dB[BQ / 4];
 
@@ -434,25 +448,29 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
   bwd::load_row(vreg, Vg, key, N, D, h, 0u);
 
   uint32_t toff[NLD];
+  bool ton[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int row = (wave * NLD + i) * RPB + lane / CPR;
-    toff[i] = row * RB + (((lane % CPR) ^ bwd::bswz<D>(row)) * 16);
+    const int kg = (lane % CPR) ^ bwd::bswz<DP>(row);
+    toff[i] = row * GRB + kg * 16;
+    ton[i] = kg < D / 8;
   }
   // query tile t: Q and dO rows, and the rows' -LSE log2(e) and Delta (the
   // first wave, 4 bytes a lane), all by buffer-to-LDS loads
   auto issue = [&](u32x4* qd, u32x4* gd, f32x4* ld, f32x4* dd, int tq) __attribute__((always_inline)) {
     const int r0 = tq * BQ;
-    const uint32_t bytes = (uint32_t)(N - r0) * RB;
+    const uint32_t bytes = (uint32_t)(N - r0) * GRB;
     const __amdgpu_buffer_rsrc_t rq =
         __builtin_amdgcn_make_buffer_rsrc((void*)(Qg + (size_t)r0 * D), (short)0, (int)bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rg =
         __builtin_amdgcn_make_buffer_rsrc((void*)(dOg + (size_t)r0 * D), (short)0, (int)bytes, kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      lds_load16(rq, qd + (wave * NLD + i) * 64, toff[i]);
-      lds_load16(rg, gd + (wave * NLD + i) * 64, toff[i]);
-    }
+    for (int i = 0; i < NLD; ++i)
+      if (D == DP || ton[i]) {
+        lds_load16(rq, qd + (wave * NLD + i) * 64, toff[i]);
+        lds_load16(rg, gd + (wave * NLD + i) * 64, toff[i]);
+      }
     if (wave == 0) {
       const uint32_t fbytes = (uint32_t)(N - r0) * 4;
       const __amdgpu_buffer_rsrc_t rl =
@@ -473,12 +491,12 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
   // operand of score slot f: rows of block f / (2 NKK), chunk (f / 2) % NKK of
   // Q (even f: S) or dO (odd f: dP); of gradient slot f: step f / (2 NDB),
   // d block (f / 2) % NDB of dO^T (even f: dV) or Q^T (odd f: dK)
-  const uint32_t rbase = bwd::row_base<D>(c32, h), tb0 = bwd::tr_base<D>(lane, 0), tb1 = bwd::tr_base<D>(lane, 1);
+  const uint32_t rbase = bwd::row_base<DP>(c32, h), tb0 = bwd::tr_base<DP>(lane, 0), tb1 = bwd::tr_base<DP>(lane, 1);
   auto sfrag = [&](const u32x4* Qt, const u32x4* Gt, int f) __attribute__((always_inline)) {
-    return bwd::row_frag<D>((f & 1) ? Gt : Qt, rbase, f / (2 * NKK), (f / 2) % NKK);
+    return bwd::row_frag<DP>((f & 1) ? Gt : Qt, rbase, f / (2 * NKK), (f / 2) % NKK);
   };
   auto gfrag = [&](const u32x4* Qt, const u32x4* Gt, int f) __attribute__((always_inline)) {
-    return bwd::tr_frag<D>((f & 1) ? Qt : Gt, tb0, tb1, (f / 2) % NDB, f / (2 * NDB));
+    return bwd::tr_frag<DP>((f & 1) ? Qt : Gt, tb0, tb1, (f / 2) % NDB, f / (2 * NDB));
   };
 
   auto compute = [&](const u32x4* Qt, const u32x4* Gt, const f32x4* Lt, const f32x4* Dt, int tq)
@@ -547,7 +565,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
       if (k == NSS / 2) mask_block(0);
       if (k >= NSS / 2)
 #pragma unroll
-        for (int e = 0; e < EPS; ++e) softmax_elem(0, (k - NSS / 2) * EPS + e);
+        for (int e = (k - HS) * 16 / HS; e < (k - HS + 1) * 16 / HS; ++e) softmax_elem(0, e);
       __builtin_amdgcn_sched_barrier(0);
     }
     // gradient phase
@@ -562,7 +580,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
       if (k == 0) mask_block(1);
       if (k < NSG / 2)
 #pragma unroll
-        for (int e = 0; e < EPG; ++e) softmax_elem(1, k * EPG + e);
+        for (int e = k * 16 / HG; e < (k + 1) * 16 / HG; ++e) softmax_elem(1, e);
       __builtin_amdgcn_sched_barrier(0);
     }
   };

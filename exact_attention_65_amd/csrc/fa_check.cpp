@@ -175,7 +175,8 @@ fa_status check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
   sz.workspace_bytes = 2 * sz.lse_bytes;  // Delta and -LSE log2(e) per row
   if (sizes) *sizes = sz;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
-  return check_supported(B, H, N, D);
+  if (D == 256) return FA_ERR_UNSUPPORTED;  // the backward: D in {64, 96, 128}
+  return check_supported(B, H, N, D, true);
 }
 
 fa_status check_bwd_call(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -282,7 +283,8 @@ __attribute__((visibility("default"))) const char* fa_status_str(fa_status s) {
     case FA_ERR_ALIASING: return "FA_ERR_ALIASING: outputs and workspace must not overlap the inputs or each other";
     case FA_ERR_UNSUPPORTED:
       return "FA_ERR_UNSUPPORTED: a head dimension or dtype the entry point lacks (D in {64,96,128,256} for 16-bit "
-             "forward inputs, {64,128} otherwise), N*D >= 2^31, more than 2^31-1 workgroups, or not a gfx950 device";
+             "forward inputs, {64,96,128} for the backward, {64,128} otherwise), N*D >= 2^31, more than 2^31-1 "
+             "workgroups, or not a gfx950 device";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call failed";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace_bytes is smaller than the call needs";
   }

@@ -216,7 +216,7 @@ fa_status fa_fwd_split_static(const void* q, const void* k, const void* v, void*
  * dout, dq, dk, dv, which share them), lse_bytes that of lse, and
  * workspace_bytes = B*H*N*8 (two floats per query row: sum_d dO O and
  * -LSE log2(e)).  Returns as fa_fwd_query; FA_ERR_UNSUPPORTED also for float32
- * (the backward takes bfloat16 and float16) and for D not in {64, 128}.
+ * (the backward takes bfloat16 and float16) and for D not in {64, 96, 128}.
  */
 fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, fa_dtype dtype,
                        fa_sizes* out);
@@ -233,8 +233,10 @@ fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, f
  * attention в 6 раз без потери точности", section "Стадии вычисления"); the
  * formulas are the derivatives of the forward.  Two kernels on `stream`: one
  * per 128 query rows (dq, and per row Delta and the LSE in base 2 into the
- * workspace), then one per 128 keys (dk, dv).  No atomics: the result is
- * deterministic.
+ * workspace), then one per 128 keys (dk, dv); when those two grids together
+ * hold at most one workgroup per compute unit, a small kernel writes Delta and
+ * the LSE in base 2 and one grid then runs both kinds of workgroup.  No
+ * atomics: the result is deterministic.
  *
  * q, k, v, o, dout : [B, H, N, D] contiguous, element type `dtype` (bfloat16
  *                    or float16), read only (may alias).
@@ -246,7 +248,7 @@ fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, f
  *                    caller-owned, clobbered.
  *
  * Validation and asynchrony as in fa_fwd; FA_ERR_WORKSPACE when
- * workspace_bytes is too small.  bfloat16 or float16, D in {64, 128}.
+ * workspace_bytes is too small.  bfloat16 or float16, D in {64, 96, 128}.
  * Allocates nothing.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

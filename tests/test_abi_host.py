@@ -95,7 +95,8 @@ def test_query_sizes():
     assert st == fa.FA_OK and sz.q_bytes == 256 * 64 * 2
     assert fa.fa_fwd_split_query(1, 1, 16, 256, 64, 1, 0, fa.FA_DTYPE_F16)[0] == fa.FA_OK
     assert fa.fa_bwd_query(1, 1, 256, 64, 0, fa.FA_DTYPE_F16)[0] == fa.FA_OK
-    assert fa.fa_bwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_F16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_F16)[0] == fa.FA_OK
+    assert fa.fa_bwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_F32)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
     assert fa.fa_fwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_F32)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_query(1, 1, 256, 80, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
@@ -210,9 +211,9 @@ def test_every_kernel_stub_is_defined():
     assert undefined == []
     kernels = set(re.findall(r"(_ZN2fa\d+fa_\w+_kernelI\w+)", out))
     # bf16 and fp16: D (64, 96, 128, 256) x causal x split; fp32: D x causal; merge: D x (bf16, fp16);
-    # backward: (bf16, fp16) x 3 kernels (dq, dk/dv, both in one grid) x D x causal and the Delta kernel
-    # (bf16, fp16) x D; fp8: D x causal; one-query-row: (bf16, fp16) x D (64, 128, 256)
-    assert len(kernels) == 32 + 4 + 8 + 24 + 4 + 4 + 6, kernels
+    # backward: (bf16, fp16) x 3 kernels (dq, dk/dv, both in one grid) x D (64, 96, 128) x causal and the
+    # Delta kernel (bf16, fp16) x D; fp8: D x causal; one-query-row: (bf16, fp16) x D (64, 128, 256)
+    assert len(kernels) == 32 + 4 + 8 + 36 + 6 + 4 + 6, kernels
 
 
 # ---------------------------------------------------------------- fa_fwd_split
@@ -329,7 +330,9 @@ def test_bwd_query_sizes():
     assert sz.q_bytes == sz.k_bytes == sz.v_bytes == sz.o_bytes == 2 * 32 * 4096 * 128 * 2
     assert sz.lse_bytes == 2 * 32 * 4096 * 4 and sz.workspace_bytes == 2 * sz.lse_bytes
     assert fa.fa_bwd_query(1, 1, 256, 64, 0, fa.FA_DTYPE_F32)[0] == fa.FA_ERR_UNSUPPORTED
-    assert fa.fa_bwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
+    assert fa.fa_bwd_query(1, 1, 256, 256, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_query(1, 1, 256, 80, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_bwd_query(1, 1, 0, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
     assert fa.fa_bwd_query(1, 1, 256, 64, 0, 9)[0] == fa.FA_ERR_BAD_DTYPE
     assert fa.lib().fa_bwd_query(1, 1, 256, 64, 0, 1, None) == fa.FA_ERR_NULL_POINTER
@@ -363,7 +366,8 @@ def bwd_call(q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, do=A + 4 * SZ, lse=A + 5
     (dict(ws=A + 8 * SZ + 16), fa.FA_ERR_ALIASING),       # workspace inside dv
     (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE),
     (dict(N=0), fa.FA_ERR_BAD_SHAPE),
-    (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=256), fa.FA_ERR_UNSUPPORTED),                 # the backward takes D in {64, 96, 128}
+    (dict(D=80), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=4), fa.FA_ERR_BAD_DTYPE),
 ])

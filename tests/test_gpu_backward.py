@@ -89,8 +89,30 @@ def test_backward_small_shapes(N, causal, D):
     _compare(w, grads, [(0, 0), (0, 1)], w.scale, f"{w.name} causal={causal}")
 
 
+D96_N = [1, 65, 200, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_backward_fused_and_separate_launches(causal):
+@pytest.mark.parametrize("N", D96_N)
+def test_backward_d96(N, causal, dtype):
+    """D = 96 (128-wide LDS rows whose last 32 columns stay zero; the MFMAs
+    cover the 96 real columns): every element of both heads, gradients
+    prefilled with NaN."""
+    w = fi.Workload(f"bwd_d96_n{N}_{dtype}", 790 + D96_N.index(N) * 4 + 2 * causal + (dtype == "f16"), 1, 2, N, 96,
+                    dtype, causal)
+    gu.log(f"[gpu] backward D=96 N={N} causal={causal} {dtype}")
+    q, k, v = gu.workload_tensors(w)
+    o, lse = fa.attention_forward(q, k, v, causal=causal, scale=w.scale)
+    g = [torch.full_like(q, float("nan")) for _ in range(3)]
+    fa.attention_backward(q, k, v, o, lse, _dout(w), causal=causal, scale=w.scale, dq=g[0], dk=g[1], dv=g[2])
+    torch.cuda.synchronize()
+    _compare(w, g, [(0, 0), (0, 1)], w.scale, f"{w.name} causal={causal}")
+
+
+@pytest.mark.parametrize("D", [96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_fused_and_separate_launches(causal, D):
     """The same heads through both launch plans: B=1, H=32, N=512 gives 128 dq
     and 128 dk/dv workgroups, one per compute unit of the 256, so fa_bwd runs
     them in one launch after the Delta kernel; H=33 gives 264 and the two
@@ -98,7 +120,7 @@ def test_backward_fused_and_separate_launches(causal):
     (b, h) and the seed, so heads 0 and 1 are the same in both."""
     results = {}
     for H in (32, 33):
-        w = fi.Workload("bwd_plans_n512_d128", 770, 1, H, 512, 128, "bf16", causal)
+        w = fi.Workload(f"bwd_plans_n512_d{D}", 770, 1, H, 512, D, "bf16", causal)
         gu.log(f"[gpu] backward N=512 H={H} causal={causal}")
         q, k, v = gu.workload_tensors(w)
         grads = _backward(w, q, k, v, _dout(w), w.scale)
@@ -198,7 +220,7 @@ def test_backward_f16_negative_scale():
     _compare(w, grads, [(0, 0), (0, 1)], -0.125, f"{w.name} scale=-0.125")
 
 
-@pytest.mark.parametrize("w", [fi.BF16_N4096, fi.CAUSAL_SWEEP[3], fi.F16_N4096], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [fi.BF16_N4096, fi.CAUSAL_SWEEP[3], fi.F16_N4096, fi.D96_N4096], ids=lambda w: w.name)
 def test_backward_full_size(w):
     """The full-size workloads, in the launch configuration the benchmark
     times; every element of seeded heads."""

@@ -74,12 +74,12 @@ def test_every_tile_barrier_drains_vmcnt(asm):
 
 def test_backward_kernels_present(bwd_asm):
     names = [n for n, _ in _kernels(bwd_asm)]
-    # (bf16, fp16) x D (64, 128) x causal for each of the three tile kernels (dq, dk/dv, both in one
-    # grid), and (bf16, fp16) x D for the Delta kernel
-    assert sum("bwd_dq" in n for n in names) == 8, names
-    assert sum("bwd_dkdv" in n for n in names) == 8, names
-    assert sum("bwd_fused" in n for n in names) == 8, names
-    assert sum("bwd_delta" in n for n in names) == 4, names
+    # (bf16, fp16) x D (64, 96, 128) x causal for each of the three tile kernels (dq, dk/dv, both in
+    # one grid), and (bf16, fp16) x D for the Delta kernel
+    assert sum("bwd_dq" in n for n in names) == 12, names
+    assert sum("bwd_dkdv" in n for n in names) == 12, names
+    assert sum("bwd_fused" in n for n in names) == 12, names
+    assert sum("bwd_delta" in n for n in names) == 6, names
 
 
 def test_backward_tile_barriers_drain_vmcnt(bwd_asm):
