@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the attention runs in the HIP
 kernels of libfa_mi355x.so.  The names mirror the C ABI (fa_fwd, fa_fwd_query,
-fa_fwd_split, fa_fwd_split_query, fa_bwd, fa_bwd_query, fa_status_str,
+fa_fwd_split, fa_fwd_split_query, fa_bwd, fa_bwd_query, fa_bwd_qk, fa_bwd_qk_query, fa_status_str,
 fa_fwd_fp8, fa_fwd_fp8_query, fa_abi_version); ``attention_forward``,
 ``attention_forward_split``, ``attention_backward`` and ``attention_forward_fp8``
 are the torch-facing helpers that allocate outputs (and
@@ -41,7 +41,8 @@ FA_SPLIT_MAX = 256
 FA_STATIC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = ("fa_fwd", "fa_fwd_query", "fa_fwd_split", "fa_fwd_split_query", "fa_fwd_split_static", "fa_bwd",
-            "fa_bwd_query", "fa_fwd_fp8", "fa_fwd_fp8_query", "fa_status_str", "fa_abi_version")
+            "fa_bwd_query", "fa_bwd_qk", "fa_bwd_qk_query", "fa_fwd_fp8", "fa_fwd_fp8_query", "fa_status_str",
+            "fa_abi_version")
 
 
 class FaSizes(ctypes.Structure):
@@ -79,6 +80,11 @@ def _load():
                            ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.fa_bwd_query.restype = ctypes.c_int
     lib.fa_bwd_query.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(FaSizes)]
+    lib.fa_bwd_qk.restype = ctypes.c_int
+    lib.fa_bwd_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64,
+                              ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+    lib.fa_bwd_qk_query.restype = ctypes.c_int
+    lib.fa_bwd_qk_query.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(FaSizes)]
     lib.fa_fwd_fp8.restype = ctypes.c_int
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp]
     lib.fa_fwd_fp8_query.restype = ctypes.c_int
@@ -147,6 +153,20 @@ def fa_bwd_query(B, H, N, D, causal, dtype):
     """Returns (status, FaSizes)."""
     sz = FaSizes()
     st = lib().fa_bwd_query(B, H, N, D, int(causal), int(dtype), ctypes.byref(sz))
+    return st, sz
+
+
+def fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Nq, Nk, D, causal, scale, dtype,
+              stream) -> int:
+    """Raw C call: pointers as integers (device addresses), returns the fa_status."""
+    return lib().fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Nq, Nk, D,
+                           int(causal), float(scale), int(dtype), stream)
+
+
+def fa_bwd_qk_query(B, H, Nq, Nk, D, causal, dtype):
+    """Returns (status, FaSizes)."""
+    sz = FaSizes()
+    st = lib().fa_bwd_qk_query(B, H, Nq, Nk, D, int(causal), int(dtype), ctypes.byref(sz))
     return st, sz
 
 
@@ -279,43 +299,53 @@ def attention_forward_split(q, k, v, causal: bool = False, scale: float | None =
 
 def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
                        dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """dq, dk, dv of attention_forward's o for the upstream gradient dout.
+    """dq, dk, dv of the forward's o for the upstream gradient dout.
 
-    q, k, v, o, dout: contiguous bf16 or fp16 GPU tensors [B, H, N, D] of one
-    dtype (the gradients have it too); o and lse as
-    attention_forward returned them for the same q, k, v, causal and scale.
-    Allocates the gradients (and the workspace, unless a uint8 GPU tensor is
-    given) with torch.  Launches on ``stream`` (default: torch's current
-    stream); no synchronisation.
+    q, o, dout: contiguous bf16 or fp16 GPU tensors [B, H, Nq, D]; k, v:
+    [B, H, Nk, D] of the same dtype (the gradients have it too).  o and lse as
+    attention_forward (Nq = Nk, fa_bwd) or attention_forward_split (fa_bwd_qk)
+    returned them for the same q, k, v, causal and scale.  Allocates the
+    gradients (and the workspace, unless a uint8 GPU tensor is given) with
+    torch.  Launches on ``stream`` (default: torch's current stream); no
+    synchronisation.
     """
     import torch
     if q.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError(f"unsupported dtype {q.dtype}")
     dt = _dtype_code(q.dtype)
-    for x in (q, k, v, o, dout):
-        if x.dtype != q.dtype or x.shape != q.shape or not x.is_cuda or not x.is_contiguous():
-            raise ValueError("q, k, v, o, dout must be contiguous GPU tensors of one shape and dtype")
-    B, H, N, D = q.shape
-    _check_given(lse, "lse", (B, H, N), torch.float32, q.device)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v, o, dout must be 4-d [B, H, N, D] tensors")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    for x, shape in ((q, (B, H, Nq, D)), (o, (B, H, Nq, D)), (dout, (B, H, Nq, D)), (k, (B, H, Nk, D)),
+                     (v, (B, H, Nk, D))):
+        if x.dtype != q.dtype or tuple(x.shape) != shape or not x.is_cuda or not x.is_contiguous():
+            raise ValueError("q, o, dout [B, H, Nq, D] and k, v [B, H, Nk, D] must be contiguous GPU tensors "
+                             "of one dtype")
+    _check_given(lse, "lse", (B, H, Nq), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    st, sz = fa_bwd_query(B, H, N, D, causal, dt)
+    square = Nq == Nk
+    st, sz = fa_bwd_query(B, H, Nq, D, causal, dt) if square else fa_bwd_qk_query(B, H, Nq, Nk, D, causal, dt)
     if st != FA_OK:
         raise FaError(st)
     dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _check_given(t, name, q.shape, q.dtype, q.device)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, name, like in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _check_given(t, name, like.shape, q.dtype, q.device)
     if workspace is None:
         workspace = torch.empty(sz.workspace_bytes, dtype=torch.uint8, device=q.device)
     _check_workspace(workspace, sz.workspace_bytes, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                workspace.numel() * workspace.element_size(), B, H, N, D, causal, scale, dt,
-                stream.cuda_stream)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size())
+    if square:
+        st = fa_bwd(*ptrs, B, H, Nq, D, causal, scale, dt, stream.cuda_stream)
+    else:
+        st = fa_bwd_qk(*ptrs, B, H, Nq, Nk, D, causal, scale, dt, stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st)
     return dq, dk, dv

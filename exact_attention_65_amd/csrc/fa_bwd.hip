@@ -21,8 +21,8 @@ namespace fa {
 namespace {
 
 template <typename Kern>
-hipError_t launch(Kern kern, const BwdArgs& a, hipStream_t s, int mult = 1) {
-  hipLaunchKernelGGL(kern, dim3(a.n_blocks * mult), dim3(kBwdThreads), 0, s, a);
+hipError_t launch(Kern kern, const BwdArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBwdThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -32,22 +32,26 @@ bool fuse_bwd(const BwdArgs& a) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  return 2LL * a.n_blocks <= cus;
+  return (int64_t)a.n_qblocks + a.n_kblocks <= cus;
 }
 
 template <typename E, int D>
 hipError_t launch_fused(bool causal, const BwdArgs& a, hipStream_t s) {
-  hipError_t e = launch(fa_bwd_delta_kernel<E, D>, a, s);
+  hipError_t e = launch(fa_bwd_delta_kernel<E, D>, a, a.n_qblocks, s);
   if (e != hipSuccess) return e;
-  return causal ? launch(fa_bwd_fused_kernel<E, D, true>, a, s, 2) : launch(fa_bwd_fused_kernel<E, D, false>, a, s, 2);
+  const int grid = a.n_kblocks + a.n_qblocks;
+  return causal ? launch(fa_bwd_fused_kernel<E, D, true>, a, grid, s)
+                : launch(fa_bwd_fused_kernel<E, D, false>, a, grid, s);
 }
 
 template <typename E, int D>
 hipError_t launch_bwd_d(bool causal, const BwdArgs& a, hipStream_t s) {
   if (fuse_bwd(a)) return launch_fused<E, D>(causal, a, s);
-  const hipError_t e = causal ? launch(fa_bwd_dq_kernel<E, D, true>, a, s) : launch(fa_bwd_dq_kernel<E, D, false>, a, s);
+  const hipError_t e = causal ? launch(fa_bwd_dq_kernel<E, D, true>, a, a.n_qblocks, s)
+                              : launch(fa_bwd_dq_kernel<E, D, false>, a, a.n_qblocks, s);
   if (e != hipSuccess) return e;
-  return causal ? launch(fa_bwd_dkdv_kernel<E, D, true>, a, s) : launch(fa_bwd_dkdv_kernel<E, D, false>, a, s);
+  return causal ? launch(fa_bwd_dkdv_kernel<E, D, true>, a, a.n_kblocks, s)
+                : launch(fa_bwd_dkdv_kernel<E, D, false>, a, a.n_kblocks, s);
 }
 
 template <typename E>
@@ -68,15 +72,14 @@ hipError_t launch_bwd(int dtype, int D, bool causal, const BwdArgs& a, float sca
 }  // namespace
 }  // namespace fa
 
-extern "C" __attribute__((visibility("default"))) fa_status fa_bwd(
-    const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
-    void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t D,
-    int causal, float scale, fa_dtype dtype, fa_stream_t stream) {
-  fa_status st = fa::check_bwd_call(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, D,
-                                    scale, (int)dtype);
-  if (st != FA_OK) return st;
-  if ((st = fa::device_check()) != FA_OK) return st;
-  fa::BwdArgs a;
+namespace fa {
+namespace {
+
+// The common call after validation: Nq queries and Nk keys per (b, h).
+fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, void* workspace, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                  int64_t D, int causal, float scale, fa_dtype dtype, fa_stream_t stream) {
+  BwdArgs a;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -87,14 +90,42 @@ extern "C" __attribute__((visibility("default"))) fa_status fa_bwd(
   a.dk = dk;
   a.dv = dv;
   a.delta = (float*)workspace;
-  a.nlse2 = a.delta + B * H * N;
-  a.n = (int)N;
-  a.n_blk = (int)((N + fa::kBwdRows - 1) / fa::kBwdRows);
-  a.n_blocks = (int)(B * H * a.n_blk);
+  a.nlse2 = a.delta + B * H * Nq;
+  a.nq = (int)Nq;
+  a.nk = (int)Nk;
+  a.n_qblk = (int)((Nq + kBwdRows - 1) / kBwdRows);
+  a.n_kblk = (int)((Nk + kBwdRows - 1) / kBwdRows);
+  a.n_qblocks = (int)(B * H * a.n_qblk);
+  a.n_kblocks = (int)(B * H * a.n_kblk);
   const float c = std::fabs(scale) * 1.44269504088896340736f;
   a.c = c < FLT_MIN ? FLT_MIN : c;
   a.scale = scale;
   a.flip = 0u;
-  const hipError_t e = fa::launch_bwd((int)dtype, (int)D, causal != 0, a, scale, (hipStream_t)stream);
+  const hipError_t e = launch_bwd((int)dtype, (int)D, causal != 0, a, scale, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace fa
+
+extern "C" __attribute__((visibility("default"))) fa_status fa_bwd(
+    const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+    void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t D,
+    int causal, float scale, fa_dtype dtype, fa_stream_t stream) {
+  fa_status st = fa::check_bwd_call(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, D,
+                                    scale, (int)dtype);
+  if (st != FA_OK) return st;
+  if ((st = fa::device_check()) != FA_OK) return st;
+  return fa::run_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, N, D, causal, scale, dtype, stream);
+}
+
+extern "C" __attribute__((visibility("default"))) fa_status fa_bwd_qk(
+    const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+    void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+    int64_t D, int causal, float scale, fa_dtype dtype, fa_stream_t stream) {
+  fa_status st = fa::check_bwd_qk_call(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Nq, Nk,
+                                       D, causal, scale, (int)dtype);
+  if (st != FA_OK) return st;
+  if ((st = fa::device_check()) != FA_OK) return st;
+  return fa::run_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk, D, causal, scale, dtype, stream);
 }

@@ -34,11 +34,13 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;      // [B*H*N] workspace: sum_d dO O per row
-  float* nlse2;      // [B*H*N] workspace: -LSE log2(e) per row
-  int n;             // sequence length N
-  int n_blk;         // 128-row blocks per (b, h)
-  int n_blocks;      // workgroups in the grid: B * H * n_blk
+  float* delta;      // [B*H*Nq] workspace: sum_d dO O per query row
+  float* nlse2;      // [B*H*Nq] workspace: -LSE log2(e) per query row
+  int nq, nk;        // queries and keys per (b, h); causal: query i is position i + nk - nq
+  int n_qblk;        // 128-row query blocks per (b, h)
+  int n_kblk;        // 128-key blocks per (b, h)
+  int n_qblocks;     // dq workgroups: B * H * n_qblk
+  int n_kblocks;     // dk/dv workgroups: B * H * n_kblk
   float c;           // |scale| * log2(e), at least FLT_MIN
   float scale;       // the signed scale, applied to dQ and dK at the end
   uint32_t flip;     // XOR on the register-held Q (dq kernel) or K (dkdv kernel) bits: sign of scale
@@ -182,8 +184,8 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_delta_kernel(BwdArgs a) {
   constexpr int NKK = D / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, c32 = lane & 31;
-  const int N = a.n;
-  const int bh = blockIdx.x / a.n_blk, qb = blockIdx.x % a.n_blk;
+  const int N = a.nq;
+  const int bh = blockIdx.x / a.n_qblk, qb = blockIdx.x % a.n_qblk;
   const int qrow = qb * kBwdRows + wave * 32 + c32;
   const size_t head = (size_t)bh * N * D;
   vec8 dof[NKK];
@@ -220,23 +222,25 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
-  const int N = a.n;
-  const HeadItem wi = head_item(xcd_remap(blk, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL, true);
+  // N: queries, NK: keys; under the causal mask key j is visible to query i
+  // iff j <= i + OFF
+  const int N = a.nq, NK = a.nk, OFF = CAUSAL ? NK - N : 0;
+  const HeadItem wi = head_item(xcd_remap(blk, a.n_qblocks), a.n_qblocks / a.n_qblk, a.n_qblk, CAUSAL, true);
   const int bh = wi.bh;
-  const int qb = CAUSAL ? a.n_blk - 1 - wi.idx : wi.idx;  // causal: longest query blocks first
+  const int qb = CAUSAL ? a.n_qblk - 1 - wi.idx : wi.idx;  // causal: longest query blocks first
   const int q0 = qb * kBwdRows;
-  const size_t head = (size_t)bh * N * D;
+  const size_t head = (size_t)bh * N * D, headk = (size_t)bh * NK * D;
   const uint16_t* Qg = (const uint16_t*)a.q + head;
-  const uint16_t* Kg = (const uint16_t*)a.k + head;
-  const uint16_t* Vg = (const uint16_t*)a.v + head;
+  const uint16_t* Kg = (const uint16_t*)a.k + headk;
+  const uint16_t* Vg = (const uint16_t*)a.v + headk;
   const uint16_t* Og = (const uint16_t*)a.o + head;
   const uint16_t* dOg = (const uint16_t*)a.dout + head;
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBwdRows) : N;
+  const int kv_end = CAUSAL ? min(NK, q0 + kBwdRows + OFF) : NK;
   const int n_tiles = (kv_end + BN - 1) / BN;
   const int qrow = q0 + wave * 32 + c32;
   const int wave_q0 = q0 + wave * 32;
-  const int n_vis = wave_q0 >= N ? 0 : CAUSAL ? min(n_tiles, (wave_q0 + 31) / BN + 1) : n_tiles;
+  const int n_vis = wave_q0 >= N ? 0 : CAUSAL ? min(n_tiles, (wave_q0 + 31 + OFF) / BN + 1) : n_tiles;
 
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -268,7 +272,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
   }
   auto issue = [&](u32x4* dst, const uint16_t* src, int kv0) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(N - kv0) * GRB), kRsrcWord3);
+        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(NK - kv0) * GRB), kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
       if (D == DP || kon[i]) lds_load16(r, dst + (wave * NLD + i) * 64, koff[i]);
@@ -301,13 +305,13 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
     constexpr int HS = NSS / 2, HG = NSG / 2;
     static_assert(HS <= 16 && HG <= 16 && NKB == 2, "slot layout");
     const int kv0 = j * BN;
-    const bool masked = kv0 + BN > N || (CAUSAL && kv0 + BN - 1 > wave_q0);
+    const bool masked = kv0 + BN > NK || (CAUSAL && kv0 + BN - 1 > wave_q0 + OFF);
     f32x16 s[NKB], dp[NKB];
     vec8 dsf[NCC];
     // element (kb, i) holds key kv0 + 32kb + 8h + kofs(i) of query qrow
     auto mask_block = [&](int kb) __attribute__((always_inline)) {
       if (masked) {
-        const int lim = (CAUSAL ? min(N - 1, qrow) : N - 1) - kv0 - 8 * h;
+        const int lim = (CAUSAL ? min(NK - 1, qrow + OFF) : NK - 1) - kv0 - 8 * h;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kofs = 32 * kb + 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
@@ -417,15 +421,17 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
-  const int N = a.n;
-  const HeadItem wi = head_item(xcd_remap(blk, a.n_blocks), a.n_blocks / a.n_blk, a.n_blk, CAUSAL, false);
+  // N: queries, NK: keys; under the causal mask key j is visible to query i
+  // iff i + OFF >= j
+  const int N = a.nq, NK = a.nk, OFF = CAUSAL ? NK - N : 0;
+  const HeadItem wi = head_item(xcd_remap(blk, a.n_kblocks), a.n_kblocks / a.n_kblk, a.n_kblk, CAUSAL, false);
   const int bh = wi.bh;
   const int kblk = wi.idx;  // causal: the first key blocks see the most queries
   const int k0 = kblk * kBwdRows;
-  const size_t head = (size_t)bh * N * D;
+  const size_t head = (size_t)bh * N * D, headk = (size_t)bh * NK * D;
   const uint16_t* Qg = (const uint16_t*)a.q + head;
-  const uint16_t* Kg = (const uint16_t*)a.k + head;
-  const uint16_t* Vg = (const uint16_t*)a.v + head;
+  const uint16_t* Kg = (const uint16_t*)a.k + headk;
+  const uint16_t* Vg = (const uint16_t*)a.v + headk;
   const uint16_t* dOg = (const uint16_t*)a.dout + head;
   const float* Lg = a.nlse2 + (size_t)bh * N;
   const float* Dg = a.delta + (size_t)bh * N;
@@ -433,9 +439,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
   const int key = k0 + wave * 32 + c32;  // this lane's key
   const int wave_k0 = k0 + wave * 32;
   const int n_qt = (N + BQ - 1) / BQ;
-  const int t_first = CAUSAL ? k0 / BQ : 0;           // first query tile with a query >= k0
-  const int t_wave = CAUSAL ? wave_k0 / BQ : 0;       // first one with a query >= this wave's keys
-  const bool active = wave_k0 < N;
+  const int t_first = CAUSAL ? max(0, k0 - OFF) / BQ : 0;      // first query tile seeing key k0
+  const int t_wave = CAUSAL ? max(0, wave_k0 - OFF) / BQ : 0;  // first one seeing this wave's first key
+  const bool active = wave_k0 < NK;
 
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -444,8 +450,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
 
   // this lane's key: K (signs flipped for a negative scale) and V as MFMA B fragments
   vec8 kreg[NKK], vreg[NKK];
-  bwd::load_row(kreg, Kg, key, N, D, h, a.flip);
-  bwd::load_row(vreg, Vg, key, N, D, h, 0u);
+  bwd::load_row(kreg, Kg, key, NK, D, h, a.flip);
+  bwd::load_row(vreg, Vg, key, NK, D, h, 0u);
 
   uint32_t toff[NLD];
   bool ton[NLD];
@@ -502,7 +508,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
   auto compute = [&](const u32x4* Qt, const u32x4* Gt, const f32x4* Lt, const f32x4* Dt, int tq)
       __attribute__((always_inline)) {
     // tiles with a query past N or (causal) before one of the wave's keys
-    const bool masked = (CAUSAL && tq * BQ < wave_k0 + 31) || tq * BQ + BQ > N;
+    const bool masked = (CAUSAL && tq * BQ + OFF < wave_k0 + 31) || tq * BQ + BQ > N;
     const float c = a.c;
     f32x16 s[NKB], dp[NKB];
     vec8 pf[NCC], dsf[NCC];
@@ -527,7 +533,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qg = tq * BQ + 4 * q4_of(kb, i) + (i & 3);
-          if (qg >= N || (CAUSAL && qg < key)) s[kb][i] = neg_inf();
+          if (qg >= N || (CAUSAL && qg + OFF < key)) s[kb][i] = neg_inf();
         }
       }
     };
@@ -599,9 +605,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
     if (tq + 1 < n_qt) step(tq + 1, qB, gB, lB, dB, qA, gA, lA, dA);
   }
 
-  if (key < N) {
-    bwd::store_rows<E>((uint16_t*)a.dk + head + (size_t)key * D, dka, h, a.scale);
-    bwd::store_rows<E>((uint16_t*)a.dv + head + (size_t)key * D, dva, h, 1.0f);
+  if (key < NK) {
+    bwd::store_rows<E>((uint16_t*)a.dk + headk + (size_t)key * D, dka, h, a.scale);
+    bwd::store_rows<E>((uint16_t*)a.dv + headk + (size_t)key * D, dva, h, 1.0f);
   }
 }
 
@@ -611,8 +617,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// dk/dv and dq workgroups in one launch (the first n_blocks workgroups are
-// dk/dv ones, the next n_blocks dq ones), after fa_bwd_delta_kernel: for grids
+// dk/dv and dq workgroups in one launch (the first n_kblocks workgroups are
+// dk/dv ones, the next n_qblocks dq ones), after fa_bwd_delta_kernel: for grids
 // that leave most compute units idle, where each kernel's time is the walk of
 // its longest workgroup over the tiles and the two walks can run side by side
 // instead of one after the other.  The two are independent given Delta and
@@ -620,8 +626,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
 // bodies' LDS).
 template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_fused_kernel(BwdArgs a) {
-  if ((int)blockIdx.x < a.n_blocks) bwd_dkdv_body<E, D, CAUSAL>(a, blockIdx.x);
-  else bwd_dq_body<E, D, CAUSAL, false>(a, (int)blockIdx.x - a.n_blocks);
+  if ((int)blockIdx.x < a.n_kblocks) bwd_dkdv_body<E, D, CAUSAL>(a, blockIdx.x);
+  else bwd_dq_body<E, D, CAUSAL, false>(a, (int)blockIdx.x - a.n_kblocks);
 }
 
 }  // namespace fa

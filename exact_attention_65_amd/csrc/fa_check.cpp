@@ -168,24 +168,47 @@ fa_status check_split_call(const void* q, const void* k, const void* v, const vo
   return FA_OK;
 }
 
-fa_status check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, fa_sizes* sizes) {
-  fa_sizes sz;
-  fa_status st = check_shape(B, H, N, D, dtype, &sz);
-  if (st != FA_OK) return st;
-  sz.workspace_bytes = 2 * sz.lse_bytes;  // Delta and -LSE log2(e) per row
-  if (sizes) *sizes = sz;
+fa_status check_bwd_qk_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, int dtype,
+                             fa_sizes* sizes) {
+  const size_t elt = elem_size(dtype);
+  if (elt == 0) return FA_ERR_BAD_DTYPE;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || D <= 0) return FA_ERR_BAD_SHAPE;
+  if (causal && Nq > Nk) return FA_ERR_BAD_SHAPE;
+  uint64_t bh, qrows, krows, qel, kel, qbytes, kbytes, lbytes, wbytes;
+  if (!mul_ok((uint64_t)B, (uint64_t)H, &bh) || !mul_ok(bh, (uint64_t)Nq, &qrows) ||
+      !mul_ok(bh, (uint64_t)Nk, &krows) || !mul_ok(qrows, (uint64_t)D, &qel) ||
+      !mul_ok(krows, (uint64_t)D, &kel) || !mul_ok(qel, elt, &qbytes) || !mul_ok(kel, elt, &kbytes) ||
+      !mul_ok(qrows, 4, &lbytes) || !mul_ok(lbytes, 2, &wbytes))
+    return FA_ERR_BAD_SHAPE;
+  if (qbytes > (uint64_t)SIZE_MAX || kbytes > (uint64_t)SIZE_MAX || wbytes > (uint64_t)SIZE_MAX)
+    return FA_ERR_BAD_SHAPE;
+  if (sizes) {
+    sizes->q_bytes = sizes->o_bytes = (size_t)qbytes;
+    sizes->k_bytes = sizes->v_bytes = (size_t)kbytes;
+    sizes->lse_bytes = (size_t)lbytes;
+    sizes->workspace_bytes = (size_t)wbytes;  // Delta and -LSE log2(e) per query row
+  }
+  // the arguments are valid; what follows decides whether the kernels support them
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
-  if (D == 256) return FA_ERR_UNSUPPORTED;  // the backward: D in {64, 96, 128}
-  return check_supported(B, H, N, D, true);
+  if (D != 64 && D != 96 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (Nq * D > (int64_t)INT32_MAX || Nk * D > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
+  // both grids, and their sum (the one-launch plan), within the grid limit
+  const int64_t blocks = (Nq + kRowsPerBlock - 1) / kRowsPerBlock + (Nk + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (B > kMaxGrid / H || B * H > kMaxGrid / blocks) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
 }
 
-fa_status check_bwd_call(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                         const void* lse, const void* dq, const void* dk, const void* dv, const void* workspace,
-                         size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t D, float scale,
-                         int dtype) {
+fa_status check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, fa_sizes* sizes) {
+  return check_bwd_qk_shape(B, H, N, N, D, 0, dtype, sizes);
+}
+
+fa_status check_bwd_qk_call(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const void* lse, const void* dq, const void* dk, const void* dv, const void* workspace,
+                            size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                            int causal, float scale, int dtype) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL_POINTER;
   fa_sizes sz;
-  fa_status st = check_bwd_shape(B, H, N, D, dtype, &sz);
+  fa_status st = check_bwd_qk_shape(B, H, Nq, Nk, D, causal, dtype, &sz);
   if (st != FA_OK && st != FA_ERR_UNSUPPORTED) return st;
   if (!std::isfinite(scale)) return FA_ERR_BAD_SCALE;
   if (st == FA_ERR_UNSUPPORTED) return st;
@@ -195,8 +218,8 @@ fa_status check_bwd_call(const void* q, const void* k, const void* v, const void
   if (workspace_bytes < sz.workspace_bytes) return FA_ERR_WORKSPACE;
   // outputs and workspace may not overlap any buffer or each other; inputs may alias
   struct Buf { const void* p; size_t n; };
-  const Buf outs[4] = {{dq, sz.q_bytes}, {dk, sz.q_bytes}, {dv, sz.q_bytes}, {workspace, sz.workspace_bytes}};
-  const Buf ins[6] = {{q, sz.q_bytes}, {k, sz.q_bytes}, {v, sz.q_bytes}, {o, sz.q_bytes}, {dout, sz.q_bytes},
+  const Buf outs[4] = {{dq, sz.q_bytes}, {dk, sz.k_bytes}, {dv, sz.v_bytes}, {workspace, sz.workspace_bytes}};
+  const Buf ins[6] = {{q, sz.q_bytes}, {k, sz.k_bytes}, {v, sz.v_bytes}, {o, sz.o_bytes}, {dout, sz.o_bytes},
                       {lse, sz.lse_bytes}};
   for (int i = 0; i < 4; ++i) {
     for (int j = i + 1; j < 4; ++j)
@@ -205,6 +228,14 @@ fa_status check_bwd_call(const void* q, const void* k, const void* v, const void
       if (overlaps(outs[i].p, outs[i].n, b.p, b.n)) return FA_ERR_ALIASING;
   }
   return FA_OK;
+}
+
+fa_status check_bwd_call(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const void* lse, const void* dq, const void* dk, const void* dv, const void* workspace,
+                         size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t D, float scale,
+                         int dtype) {
+  return check_bwd_qk_call(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, N, D, 0, scale,
+                           dtype);
 }
 
 fa_status check_fp8_shape(int64_t B, int64_t H, int64_t N, int64_t D, fa_sizes* sizes) {
@@ -252,6 +283,13 @@ __attribute__((visibility("default"))) fa_status fa_bwd_query(int64_t B, int64_t
   (void)causal;
   if (!out) return FA_ERR_NULL_POINTER;
   return fa::check_bwd_shape(B, H, N, D, (int)dtype, out);
+}
+
+__attribute__((visibility("default"))) fa_status fa_bwd_qk_query(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                                                  int64_t D, int causal, fa_dtype dtype,
+                                                                  fa_sizes* out) {
+  if (!out) return FA_ERR_NULL_POINTER;
+  return fa::check_bwd_qk_shape(B, H, Nq, Nk, D, causal, (int)dtype, out);
 }
 
 __attribute__((visibility("default"))) fa_status fa_fwd_split_query(int64_t B, int64_t H, int64_t Nq,

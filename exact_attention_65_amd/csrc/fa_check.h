@@ -41,8 +41,17 @@ fa_status check_split_call(const void* q, const void* k, const void* v, const vo
                            int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int n_splits,
                            int dtype, int* splits);
 
-// fa_bwd_query: sizes (workspace: two floats per query row).
+// fa_bwd_qk_query: sizes (workspace: two floats per query row); fa_bwd_query
+// is the Nq = Nk case.
+fa_status check_bwd_qk_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, int dtype,
+                             fa_sizes* sizes);
 fa_status check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, fa_sizes* sizes);
+
+// Full validation of an fa_bwd_qk call, without touching the device.
+fa_status check_bwd_qk_call(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const void* lse, const void* dq, const void* dk, const void* dv, const void* workspace,
+                            size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                            int causal, float scale, int dtype);
 
 // Full validation of an fa_bwd call, without touching the device.
 fa_status check_bwd_call(const void* q, const void* k, const void* v, const void* o, const void* dout,

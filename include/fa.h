@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 /* Identical to hipStream_t.  NULL means the device's null stream. */
 typedef struct ihipStream_t* fa_stream_t;
@@ -255,6 +255,43 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                  int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale, fa_dtype dtype,
                  fa_stream_t stream);
+
+/*
+ * fa_bwd_qk_query - buffer sizes of an fa_bwd_qk call.
+ *
+ * Pure host function.  q_bytes and o_bytes are the sizes of q, o (and of dout,
+ * dq) with Nq rows, k_bytes and v_bytes those of k, v (and dk, dv) with Nk rows,
+ * lse_bytes that of lse (Nq rows), workspace_bytes = B*H*Nq*8.  Returns as
+ * fa_bwd_query, and FA_ERR_BAD_SHAPE also for causal with Nq > Nk.
+ */
+fa_status fa_bwd_qk_query(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, fa_dtype dtype,
+                          fa_sizes* out);
+
+/*
+ * fa_bwd_qk - fa_bwd for Nq queries against Nk keys per (b, h): the gradients
+ * of fa_fwd_split's O (any number of key ranges) for such a shape, e.g. a
+ * chunk of new tokens attending to the keys and values kept from earlier ones
+ * ("Wie reduziert Flash Attention den Speicherverkehr während der lokalen
+ * Inferenz?", section "Weniger IO bedeutet nicht, dass der KV-Cache
+ * entfällt").  Same formulas, kernels and determinism as fa_bwd, which is its
+ * Nq = Nk case.
+ *
+ * q, o, dout, dq   : [B, H, Nq, D];  k, v, dk, dv : [B, H, Nk, D]; element type
+ *                    `dtype` (bfloat16 or float16), contiguous; dq, dk, dv
+ *                    written, not overlapping any other buffer.
+ * lse              : float32 [B, H, Nq] from fa_fwd_split with the same inputs.
+ * causal           : as in fa_fwd_split: query i is position i + Nk - Nq and
+ *                    sees keys 0 .. i + Nk - Nq (Nq <= Nk).
+ * workspace        : >= fa_bwd_qk_query's workspace_bytes, 16-byte aligned,
+ *                    caller-owned, clobbered.
+ *
+ * Validation and asynchrony as in fa_bwd.  D in {64, 96, 128}.  Allocates
+ * nothing.
+ */
+fa_status fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
+                    fa_dtype dtype, fa_stream_t stream);
 
 /*
  * fa_fwd_fp8_query - buffer sizes of an fa_fwd_fp8 call.

@@ -75,7 +75,7 @@ def test_probe_clock_from_stamps():
 
 
 def test_version_and_strings():
-    assert fa.fa_abi_version() == 6
+    assert fa.fa_abi_version() == 7
     for st in range(10):
         s = fa.fa_status_str(st)
         assert s.startswith("FA_")
@@ -375,6 +375,60 @@ def test_bwd_validation_before_any_device_call(kw, expect):
     if expect == fa.FA_ERR_HIP and gpu_visible():
         pytest.skip("valid arguments would launch on fake addresses when a GPU is visible")
     assert bwd_call(**kw) == expect
+
+
+# ---------------------------------------------------------------- fa_bwd_qk
+def test_bwd_qk_query_sizes():
+    st, sz = fa.fa_bwd_qk_query(2, 8, 500, 3000, 96, 1, fa.FA_DTYPE_F16)
+    assert st == fa.FA_OK
+    assert sz.q_bytes == sz.o_bytes == 2 * 8 * 500 * 96 * 2
+    assert sz.k_bytes == sz.v_bytes == 2 * 8 * 3000 * 96 * 2
+    assert sz.lse_bytes == 2 * 8 * 500 * 4 and sz.workspace_bytes == 2 * sz.lse_bytes
+    # the square case gives fa_bwd_query's sizes
+    a, b = fa.fa_bwd_qk_query(1, 4, 777, 777, 128, 0, fa.FA_DTYPE_BF16)[1], fa.fa_bwd_query(1, 4, 777, 128, 0,
+                                                                                               fa.FA_DTYPE_BF16)[1]
+    assert (a.q_bytes, a.k_bytes, a.lse_bytes, a.workspace_bytes) == (b.q_bytes, b.k_bytes, b.lse_bytes,
+                                                                      b.workspace_bytes)
+    # causal needs Nq <= Nk (queries are the last Nq positions); without the mask any Nq
+    assert fa.fa_bwd_qk_query(1, 1, 300, 200, 64, 1, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
+    assert fa.fa_bwd_qk_query(1, 1, 300, 200, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
+    assert fa.fa_bwd_qk_query(1, 1, 0, 200, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
+    assert fa.fa_bwd_qk_query(1, 1, 100, 200, 256, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_qk_query(1, 1, 100, 200, 64, 0, fa.FA_DTYPE_F32)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_qk_query(1, 1, 100, 200, 64, 0, 9)[0] == fa.FA_ERR_BAD_DTYPE
+    assert fa.lib().fa_bwd_qk_query(1, 1, 100, 200, 64, 0, 1, None) == fa.FA_ERR_NULL_POINTER
+
+
+QB_ = 60 * 64 * 2 * 2   # bytes of one [1, 2, 60, 64] bf16 tensor (q, o, dout, dq)
+KB_ = 100 * 64 * 2 * 2  # bytes of one [1, 2, 100, 64] bf16 tensor (k, v, dk, dv)
+WSQ = 2 * 2 * 60 * 4    # workspace of the default bwd_qk_call
+
+
+def bwd_qk_call(q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, do=A + 4 * SZ, lse=A + 5 * SZ, dq=A + 6 * SZ,
+                dk=A + 7 * SZ, dv=A + 8 * SZ, ws=A + 9 * SZ, ws_bytes=WSQ, B=1, H=2, Nq=60, Nk=100, D=64, causal=1,
+                scale=0.125, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_bwd_qk(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, Nq, Nk, D, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), fa.FA_ERR_HIP),                              # valid: fails only at the device query
+    (dict(q=0), fa.FA_ERR_NULL_POINTER),
+    (dict(ws_bytes=WSQ - 1), fa.FA_ERR_WORKSPACE),
+    (dict(dk=A + 7 * SZ + 8), fa.FA_ERR_MISALIGNED),
+    (dict(dk=A + 6 * SZ + QB_ - 16), fa.FA_ERR_ALIASING),  # dk starts in dq's last 16 bytes (dq has Nq rows)
+    (dict(dk=A + 6 * SZ + QB_), fa.FA_ERR_HIP),           # dk right after dq: valid
+    (dict(dv=A + 7 * SZ + KB_ - 16), fa.FA_ERR_ALIASING),  # dv starts in dk's last 16 bytes (dk has Nk rows)
+    (dict(dv=A + 7 * SZ + KB_), fa.FA_ERR_HIP),
+    (dict(ws=A + 5 * SZ + 2 * 60 * 4 - 16), fa.FA_ERR_ALIASING),  # workspace starts in lse's last 16 bytes
+    (dict(Nq=101), fa.FA_ERR_BAD_SHAPE),                  # causal: Nq <= Nk
+    (dict(Nq=101, causal=0, ws_bytes=2 * 2 * 101 * 4), fa.FA_ERR_HIP),
+    (dict(scale=float("inf")), fa.FA_ERR_BAD_SCALE),
+    (dict(D=256), fa.FA_ERR_UNSUPPORTED),
+])
+def test_bwd_qk_validation_before_any_device_call(kw, expect):
+    if expect == fa.FA_ERR_HIP and gpu_visible():
+        pytest.skip("valid arguments would launch on fake addresses when a GPU is visible")
+    assert bwd_qk_call(**kw) == expect
 
 
 # ---------------------------------------------------------------- fa_fwd_fp8

@@ -110,6 +110,39 @@ def test_backward_d96(N, causal, dtype):
     _compare(w, g, [(0, 0), (0, 1)], w.scale, f"{w.name} causal={causal}")
 
 
+QK_CASES = [(1, 64, 128, True), (17, 200, 64, True), (64, 1000, 128, True), (200, 333, 96, True),
+            (129, 130, 128, True), (200, 333, 128, False), (333, 200, 128, False), (1000, 64, 64, False),
+            (65, 4096, 128, True)]
+
+
+@pytest.mark.parametrize("nq,nk,D,causal", QK_CASES, ids=lambda x: str(x))
+def test_backward_qk(nq, nk, D, causal):
+    """Nq queries against Nk keys (fa_bwd_qk): under the causal mask the queries
+    are the last Nq positions.  O and LSE from fa_fwd_split; every element of
+    both heads, gradients prefilled with NaN."""
+    i = QK_CASES.index((nq, nk, D, causal))
+    w = fi.Workload(f"bwd_qk_{nq}x{nk}_d{D}", 810 + i, 1, 2, nk, D, "bf16", causal, NQ=nq)
+    gu.log(f"[gpu] backward Nq={nq} Nk={nk} D={D} causal={causal}")
+    q, k, v = gu.workload_tensors(w)
+    o, lse = fa.attention_forward_split(q, k, v, causal=causal, scale=w.scale)
+    dq, dk, dv = torch.full_like(q, float("nan")), torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    fa.attention_backward(q, k, v, o, lse, _dout(w), causal=causal, scale=w.scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    _compare(w, (dq, dk, dv), [(0, 0), (0, 1)], w.scale, f"{w.name} causal={causal}")
+
+
+def test_backward_qk_separate_launches():
+    """A grid too large for the one-launch plan (B=1 H=48: 192 dq and 576 dk/dv
+    workgroups), Nq = 512 queries after 1024 cached keys, causal."""
+    w = fi.Workload("bwd_qk_512x1536_d128", 830, 1, 48, 1536, 128, "bf16", True, NQ=512)
+    gu.log(f"[gpu] backward {w.name}")
+    q, k, v = gu.workload_tensors(w)
+    o, lse = fa.attention_forward_split(q, k, v, causal=True, scale=w.scale)
+    grads = fa.attention_backward(q, k, v, o, lse, _dout(w), causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    _compare(w, grads, [(0, 0), (0, 47)], w.scale, w.name)
+
+
 @pytest.mark.parametrize("D", [96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_fused_and_separate_launches(causal, D):
