@@ -316,7 +316,7 @@ __global__ __launch_bounds__(kFp8Threads, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
         pend = true;
         pend_alpha = alpha;
         mu = m_new == neg_inf() ? 0.0f : m_new;
-        thr = (m_new + kTau) / c;
+        thr = (m_new + BF16::kTau) / c;  // P is bf16, as in the bf16 kernel
       }
       pin(mu);
       pin(pend_alpha);

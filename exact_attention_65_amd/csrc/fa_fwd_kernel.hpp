@@ -31,7 +31,8 @@
 //     rows hit distinct banks.  Tiles are double buffered and loaded (global to
 //     LDS, no registers) while the previous tile is consumed.
 //   * The running reference max moves only when a row's tile max exceeds it by
-//     more than kTau (log2 units), so the output rescale is rare; the final
+//     more than a headroom (kTau log2 units: 8 for the fp32 kernel and fp16 P,
+//     32 for bf16 P), so the output rescale is rare; the final
 //     o / l and LSE = (m + log2 l) ln 2 are exact for any reference <= max.
 //
 // Scale: scores are multiplied by c = |scale| * log2(e) and exponentiated with
@@ -164,6 +165,12 @@ struct BF16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
   static constexpr uint32_t kOnes2 = 0x3F803F80u;  // two bf16 ones
+  // log2 headroom of the lazy reference: weights up to 2^kTau.  bf16 has fp32's
+  // exponent range, so a wide headroom costs no precision and leaves the
+  // rescale to rows whose max climbs by more than 2^32 (it fired on a few
+  // percent of the tiles of 16x scores at 8); o stays finite while
+  // N 2^32 max|v| does.
+  static constexpr float kTau = 32.0f;
   __device__ static __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -182,6 +189,7 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
   static constexpr uint32_t kOnes2 = 0x3C003C00u;  // two fp16 ones
+  static constexpr float kTau = 8.0f;  // fp16 weights stay far below fp16's maximum, 65504
   __device__ static __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
@@ -504,7 +512,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   f32x4 lsacc = {0.0f, 0.0f, 0.0f, 0.0f};
   const uint32_t one2 = (lane == 0 || lane == 32 || lane == 17 || lane == 49) ? E::kOnes2 : 0u;
   const vec8 ones_op = __builtin_bit_cast(vec8, u32x4{one2, one2, one2, one2});
-  // raw tile maxima above thr move the reference: c thr = m_ref + kTau (-inf
+  // raw tile maxima above thr move the reference: c thr = m_ref + E::kTau (-inf
   // until a key is seen; +inf when that overflows, at the smallest c, where
   // every c s is too small to move it)
   float thr = neg_inf();
@@ -559,7 +567,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
         pend = true;
         pend_alpha = alpha;
         mu = m_new == neg_inf() ? 0.0f : m_new;
-        thr = (m_new + kTau) / c;  // a division in the rare path: no register for 1/c
+        thr = (m_new + E::kTau) / c;  // a division in the rare path: no register for 1/c
       }
       pin(mu);
       pin(pend_alpha);
