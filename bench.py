@@ -411,7 +411,7 @@ def main():
             "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "Nq": w.nq, "D": w.D,
                        "causal": w.causal, "scale": w.scale, "parallelism": "single GPU",
                        "entry_point": "fa_fwd_fp8 (E4M3 with MX block scales)" if w.dtype == "fp8" else
-                       "fa_bwd (dq kernel + dk/dv kernel)" if args.backward else
+                       "fa_bwd (dq and dk/dv kernels, or both in one grid for small grids)" if args.backward else
                        "fa_fwd" if split is None else f"fa_fwd_split ({n_ranges} key ranges)",
                        "pct_of_peak": round(100 * tflops / peak, 2),
                        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
