@@ -8,7 +8,8 @@ namespace fa {
 
 // Largest number of workgroups one launch may use (grid x dimension).
 constexpr int64_t kMaxGrid = 2147483647;
-// Query rows per workgroup of every kernel.
+// Query rows per workgroup of the kernels the grid limit is checked for (the
+// 64-row kernel for small grids runs only grids far below the limit).
 constexpr int64_t kRowsPerBlock = 128;
 
 // Element size of a dtype, 0 if the dtype is unknown.

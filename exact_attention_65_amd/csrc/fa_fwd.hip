@@ -24,6 +24,7 @@
 #include "fa_device.h"
 #include "fa_decode_kernel.hpp"
 #include "fa_fwd_kernel.hpp"
+#include "fa_fwd_rows16_kernel.hpp"
 
 namespace fa {
 namespace {
@@ -73,6 +74,49 @@ hipError_t launch_h16(int dtype, int D, bool causal, const FwdArgs& a, hipStream
                               : launch(fa_fwd_bf16_kernel<128, false, SPLIT>, n, a, t, s);
   return causal ? launch(fa_fwd_bf16_kernel<64, true, SPLIT>, n, a, t, s)
                 : launch(fa_fwd_bf16_kernel<64, false, SPLIT>, n, a, t, s);
+}
+
+// Compute units of the current device, looked up once per device (0 if the
+// lookup fails).
+std::atomic<int> g_cus[kMaxDevices];
+int cu_count() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = g_cus[dev].load(std::memory_order_acquire);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    g_cus[dev].store(n, std::memory_order_release);
+  }
+  return n;
+}
+
+// Whether a one-range 16-bit launch at D = 128 goes to the 16-row-wave kernel:
+// when its 128-row grid (a, made for 128 rows) holds at most one workgroup per
+// compute unit.  There each wave's latency per tile sets the time, and halving
+// a wave's rows per tile wins; on larger grids the 128-row kernel's larger
+// MFMA tiles read LDS half as often per query and win.
+bool use_rows16(int dtype, int D, const FwdArgs& a) {
+  return dtype != FA_DTYPE_F32 && D == 128 && a.n_split == 1 && a.n_blocks <= cu_count();
+}
+
+// The 16-row-wave kernel for arguments made for 128-row blocks: 64-row blocks
+// of the same rows.
+hipError_t launch_rows16(int dtype, bool causal, FwdArgs a, hipStream_t s) {
+  a.n_qblk = (a.nq + kRows16Rows - 1) / kRows16Rows;
+  a.n_blocks = a.n_bh * a.n_qblk;
+  const int t = kRows16Threads, n = a.n_blocks;
+  if (dtype == FA_DTYPE_F16)
+    return causal ? launch(fa_fwd_f16_rows16_kernel<true>, n, a, t, s)
+                  : launch(fa_fwd_f16_rows16_kernel<false>, n, a, t, s);
+  return causal ? launch(fa_fwd_bf16_rows16_kernel<true>, n, a, t, s)
+                : launch(fa_fwd_bf16_rows16_kernel<false>, n, a, t, s);
+}
+
+// One-range 16-bit launch: the 16-row-wave kernel on small grids at D = 128,
+// else the 128-row kernel.
+hipError_t launch_h16_one(int dtype, int D, bool causal, const FwdArgs& a, hipStream_t s) {
+  if (use_rows16(dtype, D, a)) return launch_rows16(dtype, causal, a, s);
+  return launch_h16<false>(dtype, D, causal, a, s);
 }
 
 // fp32 attention kernel; 256 threads and 128 query rows per workgroup
@@ -188,7 +232,7 @@ extern "C" __attribute__((visibility("default"))) fa_status fa_fwd(
   const fa::FwdArgs a =
       fa::make_args(q, k, v, o, lse, B, H, N, N, scale, (int)dtype, h16 ? fa::kBF16Rows : fa::kBM, 1);
   const hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = h16 ? fa::launch_h16<false>((int)dtype, (int)D, causal != 0, a, s)
+  const hipError_t e = h16 ? fa::launch_h16_one((int)dtype, (int)D, causal != 0, a, s)
                            : fa::launch_f32((int)D, causal != 0, a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -216,7 +260,7 @@ extern "C" __attribute__((visibility("default"))) fa_status fa_fwd_split(
     return fa::launch_combine((int)dtype, (int)D, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
   if (splits == 1)
-    return fa::launch_h16<false>((int)dtype, (int)D, causal != 0, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return fa::launch_h16_one((int)dtype, (int)D, causal != 0, a, s) == hipSuccess ? FA_OK : FA_ERR_HIP;
   // workspace: [splits][B*H][Nq][D] float outputs, then [splits][B*H][Nq] log-sum-exps
   a.o_part = (float*)workspace;
   a.lse_part = a.o_part + (size_t)splits * a.n_bh * a.nq * D;

@@ -108,6 +108,13 @@ fa_status fa_fwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal,
  *           valid.
  * stream  : HIP stream the single kernel launch is enqueued on.
  *
+ * The kernel takes 128 query rows per workgroup; for bfloat16 and float16 at
+ * D = 128 a grid of at most one such workgroup per compute unit
+ * (B * H * ceil(N / 128) <= the device's CU count) runs instead on a kernel of
+ * 64 rows per workgroup and 16 per wave, whose waves finish each key tile in
+ * about half the time.  Both give the same results up to the order of the
+ * fp32 additions behind the LSE.
+ *
  * The caller owns every buffer; the call allocates nothing (workspace 0).
  * Arguments are validated on the host before anything is enqueued and an
  * error is returned synchronously, with nothing launched: NULL pointers,
@@ -115,8 +122,8 @@ fa_status fa_fwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal,
  * aligned, o/lse overlapping an input or each other, unsupported shapes,
  * non-gfx950 devices.  FA_OK means the kernel was enqueued; execution is
  * asynchronous and a fault during execution surfaces at the caller's next
- * synchronisation.  Thread-safe; the only global state is a per-device
- * architecture cache.
+ * synchronisation.  Thread-safe; the only global state is a per-device cache
+ * of the architecture and the compute-unit count.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
@@ -173,7 +180,8 @@ fa_status fa_fwd_split_query(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
  *             ordered (same stream or synchronised).
  * causal    : as in fa_fwd, with the queries as the last Nq positions (Nq <= Nk).
  * n_splits  : FA_SPLIT_AUTO or 1 .. FA_SPLIT_MAX.  With one range no workspace
- *             is used and a single kernel writes o and lse.
+ *             is used and a single kernel writes o and lse (chosen as in
+ *             fa_fwd, with B * H * ceil(Nq / 128) for the grid).
  *
  * Validation and asynchrony as in fa_fwd; FA_ERR_WORKSPACE when workspace_bytes
  * is too small.  bfloat16 or float16 (not float32).  Allocates nothing.
