@@ -92,7 +92,7 @@ int cu_count() {
 
 // Whether a one-range 16-bit launch at D = 128 goes to the 16-row-wave kernel:
 // when its 128-row grid (a, made for 128 rows) holds at most one workgroup per
-// compute unit.  There each wave's latency per tile sets the time, and halving
+// compute unit.  There a wave's time per tile sets the kernel's, and halving
 // a wave's rows per tile wins; on larger grids the 128-row kernel's larger
 // MFMA tiles read LDS half as often per query and win.
 bool use_rows16(int dtype, int D, const FwdArgs& a) {
@@ -100,22 +100,28 @@ bool use_rows16(int dtype, int D, const FwdArgs& a) {
 }
 
 // The 16-row-wave kernel for arguments made for 128-row blocks: 64-row blocks
-// of the same rows.
+// of the same rows, KS waves per 16-row slice.
+template <int KS>
 hipError_t launch_rows16(int dtype, bool causal, FwdArgs a, hipStream_t s) {
   a.n_qblk = (a.nq + kRows16Rows - 1) / kRows16Rows;
   a.n_blocks = a.n_bh * a.n_qblk;
-  const int t = kRows16Threads, n = a.n_blocks;
+  const int t = 256 * KS, n = a.n_blocks;
   if (dtype == FA_DTYPE_F16)
-    return causal ? launch(fa_fwd_f16_rows16_kernel<true>, n, a, t, s)
-                  : launch(fa_fwd_f16_rows16_kernel<false>, n, a, t, s);
-  return causal ? launch(fa_fwd_bf16_rows16_kernel<true>, n, a, t, s)
-                : launch(fa_fwd_bf16_rows16_kernel<false>, n, a, t, s);
+    return causal ? launch(fa_fwd_f16_rows16_kernel<true, KS>, n, a, t, s)
+                  : launch(fa_fwd_f16_rows16_kernel<false, KS>, n, a, t, s);
+  return causal ? launch(fa_fwd_bf16_rows16_kernel<true, KS>, n, a, t, s)
+                : launch(fa_fwd_bf16_rows16_kernel<false, KS>, n, a, t, s);
 }
 
-// One-range 16-bit launch: the 16-row-wave kernel on small grids at D = 128,
-// else the 128-row kernel.
+// One-range 16-bit launch: on small grids at D = 128 the 16-row-wave kernel,
+// with two waves per slice when its 64-row grid fits one workgroup per CU
+// (8 waves, one workgroup per CU) and one wave per slice when it needs two
+// per CU; else the 128-row kernel.
 hipError_t launch_h16_one(int dtype, int D, bool causal, const FwdArgs& a, hipStream_t s) {
-  if (use_rows16(dtype, D, a)) return launch_rows16(dtype, causal, a, s);
+  if (use_rows16(dtype, D, a)) {
+    const int blocks64 = a.n_bh * ((a.nq + kRows16Rows - 1) / kRows16Rows);
+    return blocks64 <= cu_count() ? launch_rows16<2>(dtype, causal, a, s) : launch_rows16<1>(dtype, causal, a, s);
+  }
   return launch_h16<false>(dtype, D, causal, a, s);
 }
 

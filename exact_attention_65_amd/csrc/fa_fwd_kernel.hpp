@@ -405,13 +405,23 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   const int wave_end = CAUSAL ? min(t_hi, (wave_q0 + 31 + OFF) / BN + 1) : t_hi;
   const int n_vis = wave_q0 < NQ ? max(0, wave_end - t_lo) : 0;
 
-  // zero the tiles once: rows past N are never loaded, so they must hold finite values
-  {
+  // Tile rows past the last key are never loaded.  Their K rows give scores
+  // that the mask overwrites with -inf, whatever the LDS held; their V rows
+  // meet weight 0 in the value product, and 0 times a non-finite value is NaN,
+  // so a V buffer must hold finite values before a partial tile lands in it.
+  // One that held a full tile before does; a fresh one is zeroed, when one of
+  // the workgroup's first two tiles is partial.  At D = 96 the columns past D
+  // are never loaded either and meet zeros of Q and P: then every tile is
+  // zeroed.
+  const bool zero_tiles = D != DP || (NK % BN != 0 && NK < (t_lo + 2) * BN);
+  if (zero_tiles) {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = tid; i < TILE16; i += kBF16Threads) {
-      kA[i] = z;
-      kB[i] = z;
+      if constexpr (D != DP) {
+        kA[i] = z;
+        kB[i] = z;
+      }
       vA[i] = z;
       vB[i] = z;
     }
@@ -681,7 +691,9 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   };
 
   // ---- prologue ------------------------------------------------------------
-  __syncthreads();  // zeroed K tiles visible before any load lands
+  // zeroed tiles in place before any load lands; without them the first tile
+  // loads go out at once, in flight together with the Q loads
+  if (zero_tiles) __syncthreads();
   if (n_loc > 0) {
     issue(kA, Kg, koff, kon, t_lo * BN);
     issue(vA, Vg, voff, von, t_lo * BN);

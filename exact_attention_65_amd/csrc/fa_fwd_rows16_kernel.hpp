@@ -8,14 +8,19 @@
 //
 // When a launch holds about one 128-row workgroup per compute unit or fewer,
 // its time is the longest query block's walk over the key tiles, one tile
-// after another, each wave alone on its SIMD, so the latency of one wave's
-// tile sets the pace.  Here a workgroup holds 64 query rows (4 waves x 16):
-// each wave does half the MFMA work per tile, and the grid has twice as many
-// workgroups to spread over the chip.  On large grids the 128-row kernel stays
-// faster (its 32x32 tiles read each K and V fragment from LDS for twice as
-// many queries).  The arithmetic is the 128-row kernel's: scores, the lazy
-// reference with the same headroom, P rounded to the input type, the sum of
-// the rounded P on the matrix core and the fp32 sum for the LSE.
+// after another, each wave alone on its SIMD, so one wave's time per tile
+// sets the pace.  Here a workgroup holds 64 query rows in 4 slices of 16: each
+// wave does half the MFMA work per tile, and the grid has twice as many
+// workgroups to spread over the chip.  With KS = 2 two waves share a slice,
+// each taking half of every tile's keys, and merge their partial results at
+// the end (the exact merge of two softmax partial results over disjoint key
+// sets); the per-wave work halves again, until the K and V bytes each
+// workgroup must fetch per tile (32 KB) bound the tile time instead.  On large
+// grids the 128-row kernel stays faster (its 32x32 tiles use each K and V
+// byte fetched into a CU for twice as many queries).  The arithmetic is the
+// 128-row kernel's: scores, the lazy reference with the same headroom, P
+// rounded to the input type, the sum of the rounded P on the matrix core and
+// the fp32 sum for the LSE.
 //
 // Layouts (16x16x32: A lane l -> row l % 16, k block l / 16; B lane l -> column
 // l % 16, k block l / 16; result lane l -> rows 4 (l / 16) + i, column l % 16):
@@ -34,8 +39,7 @@
 
 namespace fa {
 
-constexpr int kRows16Rows = 64;      // query rows per workgroup
-constexpr int kRows16Threads = 256;  // 4 waves x 16 rows
+constexpr int kRows16Rows = 64;  // query rows per workgroup: 4 slices of 16
 
 namespace rows16 {
 // Key of row t of score block b of a 64-key tile.
@@ -72,7 +76,10 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 }  // namespace rows16
 
-template <typename E, bool CAUSAL>
+// KS waves per 16-row slice: with KS = 2, wave (slice, half) takes keys
+// 32 half .. 32 half + 31 of every tile, so each tile's work per wave halves
+// again, and the two halves' (reference, sums, O) are merged at the end.
+template <typename E, bool CAUSAL, int KS>
 __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   typedef typename E::vec8 vec8;
   constexpr int D = 128;
@@ -81,20 +88,24 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int RPB = 64 / CPR;          // rows per wave-wide load
   constexpr int TILE16 = BN * CPR;       // chunks per tile
-  constexpr int NLD = TILE16 / 64 / 4;   // wave-wide loads per wave per tile
-  constexpr int NKS = D / 32;            // 32-deep steps of the score contraction
-  constexpr int NKB = BN / 16;           // 16-key score blocks per tile
-  constexpr int NSA = NKS * NKB;         // score MFMAs per tile (phase A slots)
-  constexpr int NDB = D / 16;            // 16-wide d blocks of O
-  constexpr int NST = BN / 32;           // 32-key steps of the value contraction
-  constexpr int NSB = NDB * NST;         // value MFMAs per tile (phase B slots)
-  constexpr int PFA = 3, PFB = 4;        // fragment reads in flight
-  static_assert(NSA == 16 && NSB == 16 && NKB == 4, "slot counts");
+  constexpr int NT = 256 * KS;             // threads
+  constexpr int NLD = TILE16 / 64 / (4 * KS);  // wave-wide loads per wave per tile
+  constexpr int NKS = D / 32;              // 32-deep steps of the score contraction
+  constexpr int NKB = BN / 16 / KS;        // 16-key score blocks per wave and tile
+  constexpr int NSA = NKS * NKB;           // score MFMAs per wave and tile (phase A slots)
+  constexpr int NDB = D / 16;              // 16-wide d blocks of O
+  constexpr int NST = BN / 32 / KS;        // 32-key steps of the value contraction per wave
+  constexpr int NSB = NDB * NST;           // value MFMAs per wave and tile (phase B slots)
+  constexpr int PFA = 3, PFB = 4;          // fragment reads in flight
+  static_assert(KS == 1 || KS == 2, "one or two waves per slice");
+  static_assert(NSA == 16 / KS && NSB == 16 / KS && NSA / NKB == 4, "slot counts");
 
   __shared__ u32x4 kA[TILE16], kB[TILE16], vA[TILE16], vB[TILE16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slice = wave & 3, half = wave >> 2;  // half = 0 when KS = 1
+  const int kb0 = half * NKB, st0 = half * NST;  // this wave's first score block and key step
   const int g = lane >> 4, t16 = lane & 15;
   const int NQ = a.nq, NK = a.nk;
   const int OFF = CAUSAL ? NK - NQ : 0;
@@ -108,17 +119,21 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
 
   const int kv_end = CAUSAL ? min(NK, q0 + kRows16Rows + OFF) : NK;
   const int n_tiles = (kv_end + BN - 1) / BN;
-  const int qrow = q0 + wave * 16 + t16;  // this lane's query row
-  const int wave_q0 = q0 + wave * 16;
+  const int qrow = q0 + slice * 16 + t16;  // this lane's query row
+  const int wave_q0 = q0 + slice * 16;
   const int wave_end = CAUSAL ? min(n_tiles, (wave_q0 + 15 + OFF) / BN + 1) : n_tiles;
   const int n_vis = wave_q0 < NQ ? wave_end : 0;
 
-  {
+  // Tile rows past the last key are never loaded: their K rows give scores
+  // that the mask overwrites with -inf, their V rows meet weight 0, and 0
+  // times a non-finite value is NaN.  So a V buffer is zeroed when a partial
+  // tile can land in it before any full one: when one of the first two tiles
+  // is partial.
+  const bool zero_tiles = NK % BN != 0 && NK < 2 * BN;
+  if (zero_tiles) {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = tid; i < TILE16; i += kRows16Threads) {
-      kA[i] = z;
-      kB[i] = z;
+    for (int i = tid; i < TILE16; i += NT) {
       vA[i] = z;
       vB[i] = z;
     }
@@ -153,12 +168,13 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
     for (int i = 0; i < NLD; ++i) lds_load16(r, dst + (wave * NLD + i) * 64, off[i]);
   };
 
-  // K operand of score MFMA (kb, ks): row key_of(kb, t16) (whose swizzle is
-  // t16), global chunk 4 ks + g.  Since (4 ks + g) ^ t16 = (g ^ t16) ^ 4 ks, the
-  // address is one per-lane base XOR (ks << 6) plus the block's row offset.
+  // K operand of score MFMA (kb, ks) (kb counts the tile's blocks): row
+  // key_of(kb, t16) (whose swizzle is t16), global chunk 4 ks + g.  Since
+  // (4 ks + g) ^ t16 = (g ^ t16) ^ 4 ks, the address is one per-lane base XOR
+  // (ks << 6) plus the block's row offset.
   const uint32_t kaddr0 = (uint32_t)((8 * (t16 >> 2) + (t16 & 3)) * RB + ((g ^ t16) * 16));
   auto kfrag = [&](const u32x4* Kt, int m) __attribute__((always_inline)) {
-    const int ks = m / NKB, kb = m % NKB;
+    const int ks = m / NKB, kb = kb0 + m % NKB;
     return *(const u32x4*)((const char*)Kt + ((kaddr0 ^ (ks << 6)) + (32 * (kb >> 1) + 4 * (kb & 1)) * RB));
   };
   // V^T operand of value MFMA (db, st) by two transposed reads: in 16-lane
@@ -170,7 +186,7 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
     return (uint32_t)(row * RB + ((rows16::vswz(row) + (q >> 1)) * 16) + (q & 1) * 8);
   }();
   auto vfrag = [&](const u32x4* Vt, int s) __attribute__((always_inline)) {
-    const int db = s % NDB, st = s / NDB;
+    const int db = s % NDB, st = st0 + s / NDB;
     const char* p = (const char*)Vt + (vaddr0 ^ (db << 5)) + 32 * st * RB;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
     const i16x4 hi =
@@ -199,7 +215,7 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   float pend_alpha = 1.0f;
   const float c = a.c;
 
-  // element i of block kb of tile j: key j BN + key_of(kb, 4 g + i)
+  // element i of the wave's block kb of tile j: key j BN + key_of(kb0 + kb, 4 g + i)
   auto mask = [&](f32x4 (&s)[NKB], int j) __attribute__((always_inline)) {
     const int kv0 = j * BN;
     if (kv0 + BN > NK || (CAUSAL && kv0 + BN - 1 > wave_q0 + OFF)) {
@@ -208,7 +224,7 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (rows16::key_of(kb, 4 * g + i) > lim) s[kb][i] = neg_inf();
+          if (rows16::key_of(kb0 + kb, 4 * g + i) > lim) s[kb][i] = neg_inf();
     }
   };
   // row max and the reference update, in slices: 0..NKB-1 block maxima, NKB
@@ -220,7 +236,9 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
       pin(mx);
       mpart[k] = mx;
     } else {
-      float mx = vmax(vmax(mpart[0], mpart[1]), vmax(mpart[2], mpart[3]));
+      float mx = mpart[0];
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb) mx = vmax(mx, mpart[kb]);
       mx = rows16::quad_max(mx);
       if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
         const float m_new = vmax(m_ref, mx * c);
@@ -309,7 +327,9 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   };
 
   // ---- prologue ------------------------------------------------------------
-  __syncthreads();  // zeroed tiles visible before any load lands
+  // zeroed tiles in place before any load lands; without them the first tile
+  // loads go out at once, in flight together with the Q loads
+  if (zero_tiles) __syncthreads();
   if (n_tiles > 0) {
     issue(kA, Kg, koff, 0);
     issue(vA, Vg, voff, 0);
@@ -331,6 +351,8 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   }
 
   // ---- main loop: iteration j consumes S_j (in sc) and V_j ------------------
+  // It reads K_{j+1} and V_j and loads V_{j+1} and K_{j+2} into the buffers
+  // that V_{j-1} and K_j leave.
   auto iteration = [&](int j, f32x4 (&sc)[NKB], f32x4 (&sn)[NKB], const u32x4* Kn, u32x4* Kd, const u32x4* Vc,
                        u32x4* Vd) __attribute__((always_inline)) {
     // the explicit wait: at a barrier that heads a loop this compiler can drop
@@ -359,28 +381,67 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   // element into a wrong value)
   float e0 = lsacc[0];
   pin(e0);
-  const float l_tot =
-      __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(t16 << 2, __builtin_bit_cast(int, e0)));
-  const float lx_tot = rows16::quad_sum(lx);
+  float l_tot = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(t16 << 2, __builtin_bit_cast(int, e0)));
+  float lx_tot = rows16::quad_sum(lx);
+  float m_out = m_ref;
+  if constexpr (KS == 2) {
+    // The two halves of a slice hold o, l and lx against their own references
+    // mu_0, mu_1 (lane for lane the same query and columns).  With M the
+    // larger reference of the halves that saw a key, each half's terms take
+    // the factor 2^(mu_h - M) (0 for a half that saw none): the sums over all
+    // keys against M.  The tiles are free once every wave is past its last
+    // iteration; half 1 leaves its values there for half 0.  (No tile load is
+    // in flight after the last iteration; the wait states it for the barrier.)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x4* const ob = (f32x4*)(slice < 2 ? kA : kB) + (slice & 1) * (NDB * 64);
+    float* const sb = (float*)vA + slice * 3 * 64;
+    if (half == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) ob[db * 64 + lane] = o[db];
+      sb[lane] = mu;
+      sb[64 + lane] = l_tot;
+      sb[128 + lane] = lx_tot;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (half == 0) {
+      const float mu1 = sb[lane], l1 = sb[64 + lane], lx1 = sb[128 + lane];
+      const bool live0 = l_tot > 0.0f, live1 = l1 > 0.0f;
+      const float M = live0 && live1 ? vmax(mu, mu1) : live0 ? mu : mu1;
+      const float a0 = live0 ? __builtin_amdgcn_exp2f(mu - M) : 0.0f;
+      const float a1 = live1 ? __builtin_amdgcn_exp2f(mu1 - M) : 0.0f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const f32x4 o1 = ob[db * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[db][i] = __builtin_fmaf(o[db][i], a0, o1[i] * a1);
+      }
+      l_tot = __builtin_fmaf(l_tot, a0, l1 * a1);
+      lx_tot = __builtin_fmaf(lx_tot, a0, lx1 * a1);
+      m_out = M;
+    }
+  }
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (qrow < NQ) {
+  if (qrow < NQ && half == 0) {
     uint16_t* __restrict__ Og = (uint16_t*)a.o + ((size_t)bh * NQ + qrow) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const u32x2 w = {E::pack(o[db][0] * inv, o[db][1] * inv), E::pack(o[db][2] * inv, o[db][3] * inv)};
       *(u32x2*)(Og + 16 * db + 4 * g) = w;
     }
-    if (g == 0) a.lse[(size_t)bh * NQ + qrow] = l_tot > 0.0f ? (m_ref + __log2f(lx_tot)) * kLn2 : neg_inf();
+    if (g == 0) a.lse[(size_t)bh * NQ + qrow] = l_tot > 0.0f ? (m_out + __log2f(lx_tot)) * kLn2 : neg_inf();
   }
 }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(kRows16Threads, 2) void fa_fwd_bf16_rows16_kernel(FwdArgs a) {
-  fwd_rows16_body<BF16, CAUSAL>(a);
+// 256 KS threads; two workgroups per CU with one wave per slice, one with two
+template <bool CAUSAL, int KS>
+__global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void fa_fwd_bf16_rows16_kernel(FwdArgs a) {
+  fwd_rows16_body<BF16, CAUSAL, KS>(a);
 }
-template <bool CAUSAL>
-__global__ __launch_bounds__(kRows16Threads, 2) void fa_fwd_f16_rows16_kernel(FwdArgs a) {
-  fwd_rows16_body<F16, CAUSAL>(a);
+template <bool CAUSAL, int KS>
+__global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void fa_fwd_f16_rows16_kernel(FwdArgs a) {
+  fwd_rows16_body<F16, CAUSAL, KS>(a);
 }
 
 }  // namespace fa

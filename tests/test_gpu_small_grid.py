@@ -1,13 +1,16 @@
-"""The two one-range 16-bit kernels at D = 128 against the fp64 oracle.
+"""The one-range 16-bit forward at D = 128 on its three launch forms, against
+the fp64 oracle.
 
 fa_fwd (and fa_fwd_split with one range) runs grids of at most one 128-row
 workgroup per compute unit (B * H * ceil(Nq / 128) <= CU count) on a kernel
-with 64 rows per workgroup and 16 per wave, and larger grids on the 128-row
-kernel.  Each case runs the same heads twice: with H = 2, which takes the
-64-row kernel, and with H just large enough for the 128-row kernel on this
+with 64 rows per workgroup in slices of 16: with two waves per slice when its
+64-row grid fits one workgroup per CU, with one wave per slice otherwise.
+Larger grids run the 128-row kernel.  Each case runs the same heads with
+H = 2 (two waves per slice), with the smallest H for one wave per slice (when
+the shape has one) and with the smallest H for the 128-row kernel on this
 device.  A head's inputs depend only on its (b, h) and the seed, so heads 0
-and 1 are the same in both runs; both are checked against the oracle on heads
-0, 1 and the last, every row and column.
+and 1 are the same in every run; each run is checked against the oracle on
+heads 0, 1 and the last, every row and column.
 """
 import math
 
@@ -28,15 +31,21 @@ def _cus() -> int:
 
 
 def _head_counts(nq: int):
-    """H for the 64-row kernel (2) and the smallest H that takes the 128-row one."""
-    qblocks = math.ceil(nq / 128)
-    big = _cus() // qblocks + 1
-    assert 2 * qblocks <= _cus() < big * qblocks
-    return 2, big
+    """H for each launch form the shape has: two waves per slice, one wave per
+    slice, the 128-row kernel."""
+    cus = _cus()
+    b64, b128 = math.ceil(nq / 64), math.ceil(nq / 128)
+    hs = [2]
+    assert 2 * b64 <= cus
+    h1 = cus // b64 + 1
+    if h1 * b128 <= cus:
+        hs.append(h1)
+    hs.append(cus // b128 + 1)
+    return hs
 
 
 def _both_kernels(name, seed, nq, nk, dtype, causal, forward):
-    results = {}
+    results = []
     for H in _head_counts(nq):
         w = fi.Workload(f"{name}_h{H}", seed, 1, H, nk, 128, dtype, causal, NQ=nq if nq != nk else 0)
         gu.log(f"[gpu] {w.name}: Nq={nq} Nk={nk} {dtype} causal={causal}")
@@ -44,10 +53,11 @@ def _both_kernels(name, seed, nq, nk, dtype, causal, forward):
         o, lse = forward(w, q, k, v)
         torch.cuda.synchronize()
         gu.compare_heads(w, o, lse, [(0, 0), (0, 1), (0, H - 1)], what=f"{w.name} causal={causal}")
-        results[H] = (o[:, :2].float().cpu(), lse[:, :2].cpu())
-    (o0, l0), (o1, l1) = results.values()
-    gu.log(f"  heads 0-1, 64-row vs 128-row kernel: max|dO| {float((o0 - o1).abs().max()):.3e} "
-           f"max|dLSE| {float((l0 - l1).abs().max()):.3e}")
+        results.append((H, o[:, :2].float().cpu(), lse[:, :2].cpu()))
+    h0, o0, l0 = results[0]
+    for h1, o1, l1 in results[1:]:
+        gu.log(f"  heads 0-1, H={h0} vs H={h1}: max|dO| {float((o0 - o1).abs().max()):.3e} "
+               f"max|dLSE| {float((l0 - l1).abs().max()):.3e}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -93,11 +103,13 @@ def test_small_grid_unusual_scales(scale):
     gu.assert_within(err, "bf16", f"{w.name} scale={scale}")
 
 
-def test_small_grid_every_output_written():
+@pytest.mark.parametrize("B,H", [(3, 5), (2, 40)])
+def test_small_grid_every_output_written(B, H):
     """Outputs prefilled with NaN: every row of every head of a ragged small
-    grid (B = 3, H = 5, N = 200: 15 heads x 4 blocks of 64 rows) is written,
-    and two calls give the same bits."""
-    w = fi.Workload("grid_nan_b3_h5_n200", 1160, 3, 5, 200, 128, "bf16", True)
+    grid (N = 200: 4 blocks of 64 rows per head; 60 blocks take two waves per
+    slice, 320 one wave per slice) is written, and two calls give the same
+    bits."""
+    w = fi.Workload(f"grid_nan_b{B}_h{H}_n200", 1160, B, H, 200, 128, "bf16", True)
     q, k, v = gu.workload_tensors(w)
     outs = []
     for _ in range(2):
@@ -108,4 +120,4 @@ def test_small_grid_every_output_written():
         assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
         outs.append((o.clone(), lse.clone()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
-    gu.compare_heads(w, outs[0][0], outs[0][1], [(0, 0), (1, 2), (2, 4)], what=w.name)
+    gu.compare_heads(w, outs[0][0], outs[0][1], [(0, 0), (1, 2), (B - 1, H - 1)], what=w.name)
