@@ -17,9 +17,10 @@ through fa_fwd_split: the range kernel and the merge kernel, both inside the
 timed events.  Their roofline is the HBM one (GB/s of Q, K, V, O and LSE) when
 the workload's arithmetic intensity is below the machine balance.
 
-The FP8 workload (fp8_b2_h32_n4096_d128: E4M3 inputs with MX block scales)
-steps through fa_fwd_fp8; its roofline peak is the combination of the fp8 and
-bf16 MFMA peaks (Q K^T runs on the first, P V on the second).
+The FP8 workloads (fp8_b2_h32_n4096_d128 and fp8_b2_h16_n4096_d256: E4M3
+inputs with MX block scales) step through fa_fwd_fp8; their roofline peak is
+the combination of the fp8 and bf16 MFMA peaks (Q K^T runs on the first, P V
+on the second).
 
 With --backward a step is one fa_bwd call (its two kernels: dq with Delta, then
 dk and dv) for a seeded upstream gradient, O and LSE having been computed by

@@ -245,7 +245,8 @@ fa_status check_fp8_shape(int64_t B, int64_t H, int64_t N, int64_t D, fa_sizes* 
   const size_t codes = sz.q_bytes / 2;
   sz.q_bytes = sz.k_bytes = sz.v_bytes = codes;
   if (sizes) *sizes = sz;
-  return check_supported(B, H, N, D);
+  if (D == 96) return FA_ERR_UNSUPPORTED;   // D in {64, 128, 256}
+  return check_supported(B, H, N, D, true);
 }
 
 fa_status check_fp8_call(const void* q, const void* qs, const void* k, const void* ks, const void* v,
@@ -321,8 +322,8 @@ __attribute__((visibility("default"))) const char* fa_status_str(fa_status s) {
     case FA_ERR_ALIASING: return "FA_ERR_ALIASING: outputs and workspace must not overlap the inputs or each other";
     case FA_ERR_UNSUPPORTED:
       return "FA_ERR_UNSUPPORTED: a head dimension or dtype the entry point lacks (D in {64,96,128,256} for 16-bit "
-             "forward inputs, {64,96,128} for the backward, {64,128} otherwise), N*D >= 2^31, more than 2^31-1 "
-             "workgroups, or not a gfx950 device";
+             "forward inputs, {64,96,128} for the backward, {64,128,256} for FP8, {64,128} for fp32), N*D >= 2^31, "
+             "more than 2^31-1 workgroups, or not a gfx950 device";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call failed";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace_bytes is smaller than the call needs";
   }

@@ -54,7 +54,8 @@ __attribute__((visibility("default"))) fa_status fa_fwd_fp8(const void* q, const
   a.qflip = std::signbit(scale) && scale != 0.0f ? 0x80808080u : 0u;
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (D == 128) e = causal ? fa::launch(fa::fa_fwd_fp8_kernel<128, true>, a, s) : fa::launch(fa::fa_fwd_fp8_kernel<128, false>, a, s);
+  if (D == 256) e = causal ? fa::launch(fa::fa_fwd_fp8_kernel<256, true>, a, s) : fa::launch(fa::fa_fwd_fp8_kernel<256, false>, a, s);
+  else if (D == 128) e = causal ? fa::launch(fa::fa_fwd_fp8_kernel<128, true>, a, s) : fa::launch(fa::fa_fwd_fp8_kernel<128, false>, a, s);
   else e = causal ? fa::launch(fa::fa_fwd_fp8_kernel<64, true>, a, s) : fa::launch(fa::fa_fwd_fp8_kernel<64, false>, a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

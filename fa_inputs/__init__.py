@@ -108,7 +108,9 @@ SPLIT_WORKLOADS = (SPLIT_DECODE, SPLIT_CHUNK)
 # FP8 inputs at the headline shape: Q, K, V drawn like the bf16 workload's and
 # quantised to E4M3 with MX block scales (fa_inputs.fp8).
 FP8_N4096 = Workload("fp8_b2_h32_n4096_d128", 6, 2, 32, 4096, 128, "fp8", False)
-FP8_WORKLOADS = (FP8_N4096,)
+# and at head dimension 256 (the headline's element count with half the heads)
+FP8_D256_N4096 = Workload("fp8_b2_h16_n4096_d256", 10, 2, 16, 4096, 256, "fp8", False)
+FP8_WORKLOADS = (FP8_N4096, FP8_D256_N4096)
 # fp16 inputs at the headline shape
 F16_N4096 = Workload("f16_b2_h32_n4096_d128", 7, 2, 32, 4096, 128, "f16", False)
 # head dimension 256: the headline's bytes with half the heads; head dimension 96

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7
+#define FA_ABI_VERSION 8
 
 /* Identical to hipStream_t.  NULL means the device's null stream. */
 typedef struct ihipStream_t* fa_stream_t;
@@ -306,7 +306,8 @@ fa_status fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, 
  *
  * Pure host function.  q_bytes = k_bytes = v_bytes = B*H*N*D (one byte per
  * E4M3 code), o_bytes = B*H*N*D*2 (bf16), lse_bytes = B*H*N*4, no workspace.
- * Each scale array holds B*H*N*(D/32) bytes.  Returns as fa_fwd_query.
+ * Each scale array holds B*H*N*(D/32) bytes.  Returns as fa_fwd_query, with
+ * FA_ERR_UNSUPPORTED for D not in {64, 128, 256}.
  */
 fa_status fa_fwd_fp8_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, fa_sizes* out);
 
@@ -332,8 +333,8 @@ fa_status fa_fwd_fp8_query(int64_t B, int64_t H, int64_t N, int64_t D, int causa
  *
  * q, k, v, o, lse must be 16-byte aligned, the scale arrays 4-byte aligned;
  * o and lse must not overlap any input or each other (inputs may alias).
- * Validation and asynchrony as in fa_fwd.  D in {64, 128}; no workspace,
- * nothing allocated.
+ * Validation and asynchrony as in fa_fwd.  D in {64, 128, 256} (D = 256 since
+ * ABI version 8); no workspace, nothing allocated.
  */
 fa_status fa_fwd_fp8(const void* q, const void* q_scale, const void* k, const void* k_scale, const void* v,
                      const void* v_scale, void* o, float* lse, int64_t B, int64_t H, int64_t N, int64_t D,

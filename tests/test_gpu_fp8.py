@@ -79,7 +79,7 @@ def _compare(inp, o, lse, heads, causal, scale, what, rows_for=None):
 SMALL_N = [1, 17, 64, 65, 128, 129, 200, 333, 1000]
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", SMALL_N)
 def test_fp8_small_shapes(N, causal, D):
@@ -98,10 +98,12 @@ def test_fp8_other_scales(scale):
     _compare(inp, o, lse, [(0, 0), (0, 1)], True, scale, f"{w.name} scale={scale}")
 
 
-def test_fp8_block_scales_vary():
+@pytest.mark.parametrize("D", [128, 256])
+def test_fp8_block_scales_vary(D):
     """Scale codes drawn independently per block over a wide range: every
-    block's scale must reach the right products."""
-    w = fi.Workload("fp8_wide_n257_d128", 851, 1, 2, 257, 128, "fp8", False)
+    block's scale must reach the right products (at D = 256 each converting
+    lane's values span two V blocks)."""
+    w = fi.Workload(f"fp8_wide_n257_d{D}", 851, 1, 2, 257, D, "fp8", False)
     inp = _inputs(w)
     g = np.random.default_rng(851)
     # Q, K block scales over 2^-12 .. 2^-4 (scores of order one at scale 2^-7),
@@ -130,19 +132,21 @@ def test_fp8_block_scales_vary():
         assert lratio <= 1.0, f"{w.name} head {hh}: LSE error above its bound ({lratio:.3f})"
 
 
-def test_fp8_peaked_scores():
-    w = fi.Workload("fp8_peaked_n512_d128", 852, 1, 4, 512, 128, "fp8", True, fi.PEAKED)
+@pytest.mark.parametrize("D", [128, 256])
+def test_fp8_peaked_scores(D):
+    w = fi.Workload(f"fp8_peaked_n512_d{D}", 852, 1, 4, 512, D, "fp8", True, fi.PEAKED)
     inp = _inputs(w)
     o, lse = _run(inp, True, w.scale)
     _compare(inp, o, lse, [(0, h) for h in range(4)], True, w.scale, w.name)
 
 
-def test_fp8_outputs_written_and_deterministic():
-    w = fi.Workload("fp8_canary_n999_d128", 853, 2, 3, 999, 128, "fp8", True)
+@pytest.mark.parametrize("D", [128, 256])
+def test_fp8_outputs_written_and_deterministic(D):
+    w = fi.Workload(f"fp8_canary_n999_d{D}", 853, 2, 3, 999, D, "fp8", True)
     inp = _inputs(w)
     runs = []
     for _ in range(2):
-        o = torch.full((2, 3, 999, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        o = torch.full((2, 3, 999, D), float("nan"), dtype=torch.bfloat16, device="cuda")
         lse = torch.full((2, 3, 999), float("nan"), device="cuda")
         _run(inp, True, w.scale, out=o, lse=lse)
         assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
@@ -150,10 +154,10 @@ def test_fp8_outputs_written_and_deterministic():
     assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
 
 
-def test_fp8_full_size_workload():
-    """The FP8 headline-shape workload in the benchmark's launch configuration:
-    every head, every row."""
-    w = fi.FP8_N4096
+@pytest.mark.parametrize("w", fi.FP8_WORKLOADS, ids=lambda w: w.name)
+def test_fp8_full_size_workload(w):
+    """The FP8 workloads in the benchmark's launch configuration: every head,
+    every row."""
     gu.log(f"[gpu] fp8 workload {w.name}")
     inp = _inputs(w)
     o, lse = _run(inp, w.causal, w.scale)
