@@ -83,20 +83,20 @@ template <typename E, bool CAUSAL, int KS>
 __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   typedef typename E::vec8 vec8;
   constexpr int D = 128;
-  constexpr int BN = 64;                 // keys per tile
-  constexpr int RB = D * 2;              // bytes per K / V row
-  constexpr int CPR = D / 8;             // 16-byte chunks per row
-  constexpr int RPB = 64 / CPR;          // rows per wave-wide load
-  constexpr int TILE16 = BN * CPR;       // chunks per tile
-  constexpr int NT = 256 * KS;             // threads
+  constexpr int BN = 64;                       // keys per tile
+  constexpr int RB = D * 2;                    // bytes per K / V row
+  constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  constexpr int RPB = 64 / CPR;                // rows per wave-wide load
+  constexpr int TILE16 = BN * CPR;             // chunks per tile
+  constexpr int NT = 256 * KS;                 // threads
   constexpr int NLD = TILE16 / 64 / (4 * KS);  // wave-wide loads per wave per tile
-  constexpr int NKS = D / 32;              // 32-deep steps of the score contraction
-  constexpr int NKB = BN / 16 / KS;        // 16-key score blocks per wave and tile
-  constexpr int NSA = NKS * NKB;           // score MFMAs per wave and tile (phase A slots)
-  constexpr int NDB = D / 16;              // 16-wide d blocks of O
-  constexpr int NST = BN / 32 / KS;        // 32-key steps of the value contraction per wave
-  constexpr int NSB = NDB * NST;           // value MFMAs per wave and tile (phase B slots)
-  constexpr int PFA = 3, PFB = 4;          // fragment reads in flight
+  constexpr int NKS = D / 32;                  // 32-deep steps of the score contraction
+  constexpr int NKB = BN / 16 / KS;            // 16-key score blocks per wave and tile
+  constexpr int NSA = NKS * NKB;               // score MFMAs per wave and tile (phase A slots)
+  constexpr int NDB = D / 16;                  // 16-wide d blocks of O
+  constexpr int NST = BN / 32 / KS;            // 32-key steps of the value contraction per wave
+  constexpr int NSB = NDB * NST;               // value MFMAs per wave and tile (phase B slots)
+  constexpr int PFA = 3, PFB = 4;              // fragment reads in flight
   static_assert(KS == 1 || KS == 2, "one or two waves per slice");
   static_assert(NSA == 16 / KS && NSB == 16 / KS && NSA / NKB == 4, "slot counts");
 
