@@ -90,37 +90,38 @@ int cu_count() {
   return n;
 }
 
-// Whether a one-range 16-bit launch at D = 128 goes to the 16-row-wave kernel:
-// when its 128-row grid (a, made for 128 rows) holds at most one workgroup per
-// compute unit.  There a wave's time per tile sets the kernel's, and halving
-// a wave's rows per tile wins; on larger grids the 128-row kernel's larger
-// MFMA tiles read LDS half as often per query and win.
+// Whether a one-range 16-bit launch at D = 64 or 128 goes to the 16-row-wave
+// kernel: when its 128-row grid (a, made for 128 rows) holds at most one
+// workgroup per compute unit.  There a wave's time per tile sets the kernel's,
+// and halving a wave's rows per tile wins; on larger grids the 128-row
+// kernel's larger MFMA tiles read LDS half as often per query and win.
 bool use_rows16(int dtype, int D, const FwdArgs& a) {
-  return dtype != FA_DTYPE_F32 && D == 128 && a.n_split == 1 && a.n_blocks <= cu_count();
+  return dtype != FA_DTYPE_F32 && (D == 64 || D == 128) && a.n_split == 1 && a.n_blocks <= cu_count();
 }
 
 // The 16-row-wave kernel for arguments made for 128-row blocks: 64-row blocks
 // of the same rows, KS waves per 16-row slice.
-template <int KS>
+template <int D, int KS>
 hipError_t launch_rows16(int dtype, bool causal, FwdArgs a, hipStream_t s) {
   a.n_qblk = (a.nq + kRows16Rows - 1) / kRows16Rows;
   a.n_blocks = a.n_bh * a.n_qblk;
   const int t = 256 * KS, n = a.n_blocks;
   if (dtype == FA_DTYPE_F16)
-    return causal ? launch(fa_fwd_f16_rows16_kernel<true, KS>, n, a, t, s)
-                  : launch(fa_fwd_f16_rows16_kernel<false, KS>, n, a, t, s);
-  return causal ? launch(fa_fwd_bf16_rows16_kernel<true, KS>, n, a, t, s)
-                : launch(fa_fwd_bf16_rows16_kernel<false, KS>, n, a, t, s);
+    return causal ? launch(fa_fwd_f16_rows16_kernel<D, true, KS>, n, a, t, s)
+                  : launch(fa_fwd_f16_rows16_kernel<D, false, KS>, n, a, t, s);
+  return causal ? launch(fa_fwd_bf16_rows16_kernel<D, true, KS>, n, a, t, s)
+                : launch(fa_fwd_bf16_rows16_kernel<D, false, KS>, n, a, t, s);
 }
 
-// One-range 16-bit launch: on small grids at D = 128 the 16-row-wave kernel,
-// with two waves per slice when its 64-row grid fits one workgroup per CU
-// (8 waves, one workgroup per CU) and one wave per slice when it needs two
-// per CU; else the 128-row kernel.
+// One-range 16-bit launch: on small grids at D = 64 or 128 the 16-row-wave
+// kernel, with two waves per slice when its 64-row grid fits one workgroup
+// per CU (8 waves, one workgroup per CU) and one wave per slice when it needs
+// two per CU; else the 128-row kernel.
 hipError_t launch_h16_one(int dtype, int D, bool causal, const FwdArgs& a, hipStream_t s) {
   if (use_rows16(dtype, D, a)) {
-    const int blocks64 = a.n_bh * ((a.nq + kRows16Rows - 1) / kRows16Rows);
-    return blocks64 <= cu_count() ? launch_rows16<2>(dtype, causal, a, s) : launch_rows16<1>(dtype, causal, a, s);
+    const bool two = a.n_bh * ((a.nq + kRows16Rows - 1) / kRows16Rows) <= cu_count();
+    if (D == 64) return two ? launch_rows16<64, 2>(dtype, causal, a, s) : launch_rows16<64, 1>(dtype, causal, a, s);
+    return two ? launch_rows16<128, 2>(dtype, causal, a, s) : launch_rows16<128, 1>(dtype, causal, a, s);
   }
   return launch_h16<false>(dtype, D, causal, a, s);
 }

@@ -1,5 +1,5 @@
 // Exact attention forward for small grids: 16 query rows per wave on the
-// 16x16x32 MFMA (bf16 or fp16 inputs, D = 128, one key range).
+// 16x16x32 MFMA (bf16 or fp16 inputs, D = 64 or 128, one key range).
 //
 // The method is the 128-row kernel's: the tiled loop of "Flash Attention"
 // (wiki.ai-engineering.at, section "Tiling Algorithm") with the online
@@ -44,16 +44,30 @@ constexpr int kRows16Rows = 64;  // query rows per workgroup: 4 slices of 16
 namespace rows16 {
 // Key of row t of score block b of a 64-key tile.
 __device__ __forceinline__ int key_of(int b, int t) { return 32 * (b >> 1) + 8 * (t >> 2) + 4 * (b & 1) + (t & 3); }
-// XOR applied to the 16-byte chunk index of a K row: the 16 lanes of a score
-// read take rows key_of(b, 0..15) at one chunk; (row & 3) | ((row >> 3) & 3) << 2
-// is a bijection on those rows (it equals the lane's t), so they hit 16
-// different chunk positions (conflict-free whether the LDS serves 8 or 16 lanes
-// of a 16-byte read per cycle).
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+// XOR applied to the 16-byte chunk index of a K row.  The 16 lanes of a score
+// read take rows key_of(b, 0..15) at one chunk.  The swizzle reads only row
+// bits 0, 1, 3 and 4, which are the lane's t and not the block b, so a lane's
+// read addresses differ by constants.  At D = 128, (row & 3) | ((row >> 3) & 3) << 2
+// equals t: 16 different chunk positions.  At D = 64 (8 chunks, 128-byte rows)
+// the 3-bit (r1, r3, r0 ^ r4) keeps the 8 lanes of one pass over 32 banks, and
+// the 16 of one pass over 64 banks, on distinct banks (checked by a bank model).
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (D == 128) return (row & 3) | (((row >> 3) & 3) << 2);
+  else return ((row >> 1) & 1) | (((row >> 3) & 1) << 1) | (((row ^ (row >> 4)) & 1) << 2);
+}
 // XOR applied to a V row's chunk index: a transposed read takes 4 rows
-// 8g + 4x + r (r < 4) x 2 chunks per 16-lane group g; 2 ((row & 3) | (row >> 3 & 1) << 2)
-// sends the 8 rows of groups g, g + 1 to 8 different even chunk offsets.
-__device__ __forceinline__ int vswz(int row) { return 2 * ((row & 3) | (((row >> 3) & 1) << 2)); }
+// 8g + 4x + r (r < 4) x 2 chunks per 16-lane group g.  At D = 128,
+// 2 ((row & 3) | (row >> 3 & 1) << 2) sends the 8 rows of groups g, g + 1 to 8
+// different even chunk offsets; at D = 64, 2 (r1 | (r0 ^ r3) << 1) does the
+// same for the 4 offsets a 128-byte row has, with the row's parity telling the
+// 64-bank passes apart.  Both leave bit 2 of the row out (rows r and r + 4
+// share the swizzle), and the offset is even.
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  if constexpr (D == 128) return 2 * ((row & 3) | (((row >> 3) & 1) << 2));
+  else return 2 * (((row >> 1) & 1) | (((row ^ (row >> 3)) & 1) << 1));
+}
 
 // Exchanges the odd 16-lane rows of a with the even rows of b; on two copies
 // of x, a then holds x of rows 0, 0, 2, 2 and b x of rows 1, 1, 3, 3, so their
@@ -79,10 +93,9 @@ __device__ __forceinline__ float quad_sum(float x) {
 // KS waves per 16-row slice: with KS = 2, wave (slice, half) takes keys
 // 32 half .. 32 half + 31 of every tile, so each tile's work per wave halves
 // again, and the two halves' (reference, sums, O) are merged at the end.
-template <typename E, bool CAUSAL, int KS>
+template <typename E, int D, bool CAUSAL, int KS>
 __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   typedef typename E::vec8 vec8;
-  constexpr int D = 128;
   constexpr int BN = 64;                       // keys per tile
   constexpr int RB = D * 2;                    // bytes per K / V row
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
@@ -98,7 +111,8 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   constexpr int NSB = NDB * NST;               // value MFMAs per wave and tile (phase B slots)
   constexpr int PFA = 3, PFB = 4;              // fragment reads in flight
   static_assert(KS == 1 || KS == 2, "one or two waves per slice");
-  static_assert(NSA == 16 / KS && NSB == 16 / KS && NSA / NKB == 4, "slot counts");
+  static_assert(D == 64 || D == 128, "head dimensions");
+  static_assert(NKS >= 2 && NKB >= 2 && NSB > NKB, "slot layout");
 
   __shared__ u32x4 kA[TILE16], kB[TILE16], vA[TILE16], vB[TILE16];
 
@@ -157,8 +171,8 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   for (int i = 0; i < NLD; ++i) {
     const int row = (wave * NLD + i) * RPB + lane / CPR;
     const int cl = lane % CPR;
-    koff[i] = row * RB + ((cl ^ rows16::kswz(row)) * 16);
-    voff[i] = row * RB + ((cl ^ rows16::vswz(row)) * 16);
+    koff[i] = row * RB + ((cl ^ rows16::kswz<D>(row)) * 16);
+    voff[i] = row * RB + ((cl ^ rows16::vswz<D>(row)) * 16);
   }
   auto issue = [&](u32x4* dst, const uint16_t* src, const uint32_t (&off)[NLD], int kv0)
       __attribute__((always_inline)) {
@@ -169,10 +183,13 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   };
 
   // K operand of score MFMA (kb, ks) (kb counts the tile's blocks): row
-  // key_of(kb, t16) (whose swizzle is t16), global chunk 4 ks + g.  Since
-  // (4 ks + g) ^ t16 = (g ^ t16) ^ 4 ks, the address is one per-lane base XOR
-  // (ks << 6) plus the block's row offset.
-  const uint32_t kaddr0 = (uint32_t)((8 * (t16 >> 2) + (t16 & 3)) * RB + ((g ^ t16) * 16));
+  // key_of(kb, t16), whose swizzle x is that of key_of(0, t16), global chunk
+  // 4 ks + g.  Since (4 ks + g) ^ x = (g ^ x) ^ 4 ks, the address is one
+  // per-lane base XOR (ks << 6) plus the block's row offset.
+  const uint32_t kaddr0 = [&] {
+    const int row = rows16::key_of(0, t16);
+    return (uint32_t)(row * RB + ((g ^ rows16::kswz<D>(row)) * 16));
+  }();
   auto kfrag = [&](const u32x4* Kt, int m) __attribute__((always_inline)) {
     const int ks = m / NKB, kb = kb0 + m % NKB;
     return *(const u32x4*)((const char*)Kt + ((kaddr0 ^ (ks << 6)) + (32 * (kb >> 1) + 4 * (kb & 1)) * RB));
@@ -183,7 +200,7 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   const uint32_t vaddr0 = [&] {
     const int r = t16 >> 2, q = t16 & 3;
     const int row = 8 * g + r;
-    return (uint32_t)(row * RB + ((rows16::vswz(row) + (q >> 1)) * 16) + (q & 1) * 8);
+    return (uint32_t)(row * RB + ((rows16::vswz<D>(row) + (q >> 1)) * 16) + (q & 1) * 8);
   }();
   auto vfrag = [&](const u32x4* Vt, int s) __attribute__((always_inline)) {
     const int db = s % NDB, st = st0 + s / NDB;
@@ -273,7 +290,7 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   };
 
   // phase A of iteration j: score MFMAs of tile j+1 into sn beside the
-  // exponentials of tile j in sc (one block of 4 scores every 4 slots); K
+  // exponentials of tile j in sc (one block of 4 scores every NKS slots); K
   // fragments PFA slots ahead, the first value fragments in the last PFB slots
   auto phase_a = [&](f32x4 (&sc)[NKB], f32x4 (&sn)[NKB], const u32x4* Kt, const u32x4* Vc, u32x4 (&vf)[NSB])
       __attribute__((always_inline)) {
@@ -286,7 +303,7 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
     for (int k = 0; k < NSA; ++k) {
       if (k + PFA < NSA) kf[k + PFA] = kfrag(Kt, k + PFA);
       if (k >= NSA - PFB) vf[k - (NSA - PFB)] = vfrag(Vc, k - (NSA - PFB));
-      if ((k & 3) == 1) pw[k >> 2] = p_slice(sc, k >> 2);
+      if (k % NKS == 1) pw[k / NKS] = p_slice(sc, k / NKS);
       const int ks = k / NKB, kb = k % NKB;
       const f32x4 z = {};
       sn[kb] = E::mfma16(__builtin_bit_cast(vec8, kf[k]), qf[ks], ks == 0 ? z : sn[kb]);
@@ -435,13 +452,13 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
 }
 
 // 256 KS threads; two workgroups per CU with one wave per slice, one with two
-template <bool CAUSAL, int KS>
+template <int D, bool CAUSAL, int KS>
 __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void fa_fwd_bf16_rows16_kernel(FwdArgs a) {
-  fwd_rows16_body<BF16, CAUSAL, KS>(a);
+  fwd_rows16_body<BF16, D, CAUSAL, KS>(a);
 }
-template <bool CAUSAL, int KS>
+template <int D, bool CAUSAL, int KS>
 __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void fa_fwd_f16_rows16_kernel(FwdArgs a) {
-  fwd_rows16_body<F16, CAUSAL, KS>(a);
+  fwd_rows16_body<F16, D, CAUSAL, KS>(a);
 }
 
 }  // namespace fa

@@ -1,5 +1,5 @@
-"""The one-range 16-bit forward at D = 128 on its three launch forms, against
-the fp64 oracle.
+"""The one-range 16-bit forward at D = 64 and 128 on its three launch forms,
+against the fp64 oracle.
 
 fa_fwd (and fa_fwd_split with one range) runs grids of at most one 128-row
 workgroup per compute unit (B * H * ceil(Nq / 128) <= CU count) on a kernel
@@ -44,10 +44,10 @@ def _head_counts(nq: int):
     return hs
 
 
-def _both_kernels(name, seed, nq, nk, dtype, causal, forward):
+def _both_kernels(name, seed, nq, nk, dtype, causal, forward, D=128):
     results = []
     for H in _head_counts(nq):
-        w = fi.Workload(f"{name}_h{H}", seed, 1, H, nk, 128, dtype, causal, NQ=nq if nq != nk else 0)
+        w = fi.Workload(f"{name}_h{H}", seed, 1, H, nk, D, dtype, causal, NQ=nq if nq != nk else 0)
         gu.log(f"[gpu] {w.name}: Nq={nq} Nk={nk} {dtype} causal={causal}")
         q, k, v = gu.workload_tensors(w)
         o, lse = forward(w, q, k, v)
@@ -60,21 +60,23 @@ def _both_kernels(name, seed, nq, nk, dtype, causal, forward):
                f"max|dLSE| {float((l0 - l1).abs().max()):.3e}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", EDGE_N)
-def test_fwd_small_and_large_grids(N, causal, dtype):
+def test_fwd_small_and_large_grids(N, causal, dtype, D):
     seed = 1100 + 2 * EDGE_N.index(N) + causal
 
     def forward(w, q, k, v):
         return fa.attention_forward(q, k, v, causal=causal, scale=w.scale)
 
-    _both_kernels(f"grid_n{N}", seed, N, N, dtype, causal, forward)
+    _both_kernels(f"grid_n{N}_d{D}", seed, N, N, dtype, causal, forward, D)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("nq,nk", [(5, 300), (100, 1000), (257, 4096), (512, 8192)])
-def test_split_one_range_small_and_large_grids(nq, nk, causal):
+def test_split_one_range_small_and_large_grids(nq, nk, causal, D):
     """Nq queries against Nk keys (the queries are the last Nq positions under
     the causal mask) through fa_fwd_split with one range."""
     seed = 1130 + nq % 11 + causal
@@ -82,7 +84,7 @@ def test_split_one_range_small_and_large_grids(nq, nk, causal):
     def forward(w, q, k, v):
         return fa.attention_forward_split(q, k, v, causal=causal, scale=w.scale, n_splits=1)
 
-    _both_kernels(f"split1_nq{nq}_nk{nk}", seed, nq, nk, "bf16", causal, forward)
+    _both_kernels(f"split1_nq{nq}_nk{nk}_d{D}", seed, nq, nk, "bf16", causal, forward, D)
 
 
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 2.0])
@@ -103,13 +105,14 @@ def test_small_grid_unusual_scales(scale):
     gu.assert_within(err, "bf16", f"{w.name} scale={scale}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("B,H", [(3, 5), (2, 40)])
-def test_small_grid_every_output_written(B, H):
+def test_small_grid_every_output_written(B, H, D):
     """Outputs prefilled with NaN: every row of every head of a ragged small
     grid (N = 200: 4 blocks of 64 rows per head; 60 blocks take two waves per
     slice, 320 one wave per slice) is written, and two calls give the same
     bits."""
-    w = fi.Workload(f"grid_nan_b{B}_h{H}_n200", 1160, B, H, 200, 128, "bf16", True)
+    w = fi.Workload(f"grid_nan_b{B}_h{H}_n200_d{D}", 1160, B, H, 200, D, "bf16", True)
     q, k, v = gu.workload_tensors(w)
     outs = []
     for _ in range(2):
