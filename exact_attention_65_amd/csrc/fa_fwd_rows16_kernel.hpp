@@ -1,5 +1,5 @@
 // Exact attention forward for small grids: 16 query rows per wave on the
-// 16x16x32 MFMA (bf16 or fp16 inputs, D = 64 or 128, one key range).
+// 16x16x32 MFMA (bf16 or fp16 inputs, D = 64, 128 or 256, one key range).
 //
 // The method is the 128-row kernel's: the tiled loop of "Flash Attention"
 // (wiki.ai-engineering.at, section "Tiling Algorithm") with the online
@@ -48,16 +48,17 @@ __device__ __forceinline__ int key_of(int b, int t) { return 32 * (b >> 1) + 8 *
 // read take rows key_of(b, 0..15) at one chunk.  The swizzle reads only row
 // bits 0, 1, 3 and 4, which are the lane's t and not the block b, so a lane's
 // read addresses differ by constants.  At D = 128, (row & 3) | ((row >> 3) & 3) << 2
-// equals t: 16 different chunk positions.  At D = 64 (8 chunks, 128-byte rows)
+// equals t: 16 different chunk positions (the same at D = 256, whose 512-byte
+// rows put every row on the same banks).  At D = 64 (8 chunks, 128-byte rows)
 // the 3-bit (r1, r3, r0 ^ r4) keeps the 8 lanes of one pass over 32 banks, and
 // the 16 of one pass over 64 banks, on distinct banks (checked by a bank model).
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
-  if constexpr (D == 128) return (row & 3) | (((row >> 3) & 3) << 2);
+  if constexpr (D >= 128) return (row & 3) | (((row >> 3) & 3) << 2);
   else return ((row >> 1) & 1) | (((row >> 3) & 1) << 1) | (((row ^ (row >> 4)) & 1) << 2);
 }
 // XOR applied to a V row's chunk index: a transposed read takes 4 rows
-// 8g + 4x + r (r < 4) x 2 chunks per 16-lane group g.  At D = 128,
+// 8g + 4x + r (r < 4) x 2 chunks per 16-lane group g.  At D = 128 and 256,
 // 2 ((row & 3) | (row >> 3 & 1) << 2) sends the 8 rows of groups g, g + 1 to 8
 // different even chunk offsets; at D = 64, 2 (r1 | (r0 ^ r3) << 1) does the
 // same for the 4 offsets a 128-byte row has, with the row's parity telling the
@@ -65,7 +66,7 @@ __device__ __forceinline__ int kswz(int row) {
 // share the swizzle), and the offset is even.
 template <int D>
 __device__ __forceinline__ int vswz(int row) {
-  if constexpr (D == 128) return 2 * ((row & 3) | (((row >> 3) & 1) << 2));
+  if constexpr (D >= 128) return 2 * ((row & 3) | (((row >> 3) & 1) << 2));
   else return 2 * (((row >> 1) & 1) | (((row ^ (row >> 3)) & 1) << 1));
 }
 
@@ -111,7 +112,7 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   constexpr int NSB = NDB * NST;               // value MFMAs per wave and tile (phase B slots)
   constexpr int PFA = 3, PFB = 4;              // fragment reads in flight
   static_assert(KS == 1 || KS == 2, "one or two waves per slice");
-  static_assert(D == 64 || D == 128, "head dimensions");
+  static_assert(D == 64 || D == 128 || D == 256, "head dimensions");
   static_assert(NKS >= 2 && NKB >= 2 && NSB > NKB, "slot layout");
 
   __shared__ u32x4 kA[TILE16], kB[TILE16], vA[TILE16], vB[TILE16];
