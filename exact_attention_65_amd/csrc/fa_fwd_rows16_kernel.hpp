@@ -1,5 +1,6 @@
 // Exact attention forward for small grids: 16 query rows per wave on the
-// 16x16x32 MFMA (bf16 or fp16 inputs, D = 64, 128 or 256, one key range).
+// 16x16x32 MFMA (bf16 or fp16 inputs, D = 64, 96, 128 or 256, one key range;
+// D = 96 in LDS rows of 128 columns, as in the 128-row kernel).
 //
 // The method is the 128-row kernel's: the tiled loop of "Flash Attention"
 // (wiki.ai-engineering.at, section "Tiling Algorithm") with the online
@@ -98,13 +99,15 @@ template <typename E, int D, bool CAUSAL, int KS>
 __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   typedef typename E::vec8 vec8;
   constexpr int BN = 64;                       // keys per tile
-  constexpr int RB = D * 2;                    // bytes per K / V row
-  constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  constexpr int DP = D == 96 ? 128 : D;        // LDS row width (columns)
+  constexpr int RB = DP * 2;                   // bytes per K / V row in LDS
+  constexpr int GRB = D * 2;                   // bytes per K / V row in memory
+  constexpr int CPR = DP / 8;                  // 16-byte chunks per LDS row
   constexpr int RPB = 64 / CPR;                // rows per wave-wide load
   constexpr int TILE16 = BN * CPR;             // chunks per tile
   constexpr int NT = 256 * KS;                 // threads
   constexpr int NLD = TILE16 / 64 / (4 * KS);  // wave-wide loads per wave per tile
-  constexpr int NKS = D / 32;                  // 32-deep steps of the score contraction
+  constexpr int NKS = DP / 32;                 // 32-deep steps of the score contraction
   constexpr int NKB = BN / 16 / KS;            // 16-key score blocks per wave and tile
   constexpr int NSA = NKS * NKB;               // score MFMAs per wave and tile (phase A slots)
   constexpr int NDB = D / 16;                  // 16-wide d blocks of O
@@ -112,7 +115,7 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   constexpr int NSB = NDB * NST;               // value MFMAs per wave and tile (phase B slots)
   constexpr int PFA = 3, PFB = 4;              // fragment reads in flight
   static_assert(KS == 1 || KS == 2, "one or two waves per slice");
-  static_assert(D == 64 || D == 128 || D == 256, "head dimensions");
+  static_assert(D == 64 || D == 96 || D == 128 || D == 256, "head dimensions");
   static_assert(NKS >= 2 && NKB >= 2 && NSB > NKB, "slot layout");
 
   __shared__ u32x4 kA[TILE16], kB[TILE16], vA[TILE16], vB[TILE16];
@@ -143,12 +146,17 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   // that the mask overwrites with -inf, their V rows meet weight 0, and 0
   // times a non-finite value is NaN.  So a V buffer is zeroed when a partial
   // tile can land in it before any full one: when one of the first two tiles
-  // is partial.
-  const bool zero_tiles = NK % BN != 0 && NK < 2 * BN;
+  // is partial.  At D = 96 the columns past D are never loaded either, and K's
+  // meet Q's zeros: then every tile is zeroed.
+  const bool zero_tiles = D != DP || (NK % BN != 0 && NK < 2 * BN);
   if (zero_tiles) {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = tid; i < TILE16; i += NT) {
+      if constexpr (D != DP) {
+        kA[i] = z;
+        kB[i] = z;
+      }
       vA[i] = z;
       vB[i] = z;
     }
@@ -161,26 +169,35 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < NQ) x = *(const u32x4*)(Qg + (size_t)qrow * D + 32 * ks + 8 * g) ^ flip;
+      const bool col_ok = D == DP || 32 * ks + 8 * g < D;  // columns past D stay zero
+      if (qrow < NQ && col_ok) x = *(const u32x4*)(Qg + (size_t)qrow * D + 32 * ks + 8 * g) ^ flip;
       qf[ks] = __builtin_bit_cast(vec8, x);
     }
   }
 
   // tile DMA: LDS position cl of a row holds global chunk cl ^ swizzle(row)
+  // (at D = 96 the lanes whose chunk is past the row load nothing)
   uint32_t koff[NLD], voff[NLD];
+  bool kon[NLD], von[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int row = (wave * NLD + i) * RPB + lane / CPR;
     const int cl = lane % CPR;
-    koff[i] = row * RB + ((cl ^ rows16::kswz<D>(row)) * 16);
-    voff[i] = row * RB + ((cl ^ rows16::vswz<D>(row)) * 16);
+    const int kg = cl ^ rows16::kswz<DP>(row), vg = cl ^ rows16::vswz<DP>(row);
+    koff[i] = row * GRB + kg * 16;
+    voff[i] = row * GRB + vg * 16;
+    kon[i] = kg < D / 8;
+    von[i] = vg < D / 8;
   }
-  auto issue = [&](u32x4* dst, const uint16_t* src, const uint32_t (&off)[NLD], int kv0)
+  auto issue = [&](u32x4* dst, const uint16_t* src, const uint32_t (&off)[NLD], const bool (&on)[NLD], int kv0)
       __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(NK - kv0) * RB), kRsrcWord3);
+        (void*)(src + (size_t)kv0 * D), (short)0, (int)((uint32_t)(NK - kv0) * GRB), kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) lds_load16(r, dst + (wave * NLD + i) * 64, off[i]);
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (D == DP) lds_load16(r, dst + (wave * NLD + i) * 64, off[i]);
+      else if (on[i]) lds_load16(r, dst + (wave * NLD + i) * 64, off[i]);
+    }
   };
 
   // K operand of score MFMA (kb, ks) (kb counts the tile's blocks): row
@@ -189,7 +206,7 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   // per-lane base XOR (ks << 6) plus the block's row offset.
   const uint32_t kaddr0 = [&] {
     const int row = rows16::key_of(0, t16);
-    return (uint32_t)(row * RB + ((g ^ rows16::kswz<D>(row)) * 16));
+    return (uint32_t)(row * RB + ((g ^ rows16::kswz<DP>(row)) * 16));
   }();
   auto kfrag = [&](const u32x4* Kt, int m) __attribute__((always_inline)) {
     const int ks = m / NKB, kb = kb0 + m % NKB;
@@ -201,7 +218,7 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   const uint32_t vaddr0 = [&] {
     const int r = t16 >> 2, q = t16 & 3;
     const int row = 8 * g + r;
-    return (uint32_t)(row * RB + ((rows16::vswz<D>(row) + (q >> 1)) * 16) + (q & 1) * 8);
+    return (uint32_t)(row * RB + ((rows16::vswz<DP>(row) + (q >> 1)) * 16) + (q & 1) * 8);
   }();
   auto vfrag = [&](const u32x4* Vt, int s) __attribute__((always_inline)) {
     const int db = s % NDB, st = st0 + s / NDB;
@@ -349,10 +366,10 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   // loads go out at once, in flight together with the Q loads
   if (zero_tiles) __syncthreads();
   if (n_tiles > 0) {
-    issue(kA, Kg, koff, 0);
-    issue(vA, Vg, voff, 0);
+    issue(kA, Kg, koff, kon, 0);
+    issue(vA, Vg, voff, von, 0);
   }
-  if (n_tiles > 1) issue(kB, Kg, koff, BN);
+  if (n_tiles > 1) issue(kB, Kg, koff, kon, BN);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // the first two K tiles and the first V tile in LDS
   if (n_vis > 0) {
@@ -377,8 +394,8 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
     // the wait for the tile loads issued in the previous iteration
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < n_tiles) issue(Vd, Vg, voff, (j + 1) * BN);
-    if (j + 2 < n_tiles) issue(Kd, Kg, koff, (j + 2) * BN);
+    if (j + 1 < n_tiles) issue(Vd, Vg, voff, von, (j + 1) * BN);
+    if (j + 2 < n_tiles) issue(Kd, Kg, koff, kon, (j + 2) * BN);
     if (j >= n_vis) return;
     // after the wave's last visible tile the "next" scores come from whatever
     // K buffer is there and are fully masked

@@ -108,8 +108,8 @@ fa_status fa_fwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal,
  *           valid.
  * stream  : HIP stream the single kernel launch is enqueued on.
  *
- * The kernel takes 128 query rows per workgroup; for bfloat16 and float16 at
- * D = 64, 128 and 256 a grid of at most one such workgroup per compute unit
+ * The kernel takes 128 query rows per workgroup; for bfloat16 and float16 a
+ * grid of at most one such workgroup per compute unit
  * (B * H * ceil(N / 128) <= the device's CU count) runs instead on a kernel of
  * 64 rows per workgroup and 16 per wave, whose waves finish each key tile in
  * about half the time.  Both give the same results up to the order of the

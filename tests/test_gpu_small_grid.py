@@ -1,9 +1,9 @@
-"""The one-range 16-bit forward at D = 64, 128 and 256 on its launch forms,
-against the fp64 oracle.
+"""The one-range 16-bit forward at D = 64, 96, 128 and 256 on its launch
+forms, against the fp64 oracle.
 
 fa_fwd (and fa_fwd_split with one range) runs grids of at most one 128-row
 workgroup per compute unit (B * H * ceil(Nq / 128) <= CU count) on a kernel
-with 64 rows per workgroup in slices of 16: at D = 64 and 128 with two waves
+with 64 rows per workgroup in slices of 16: at D = 64, 96 and 128 with two waves
 per slice when its 64-row grid fits one workgroup per CU and one wave per
 slice otherwise, at D = 256 always with two.  Larger grids run the 128-row
 kernel.  Each case runs the same heads with H = 2 (two waves per slice), with
@@ -61,7 +61,7 @@ def _both_kernels(name, seed, nq, nk, dtype, causal, forward, D=128):
                f"max|dLSE| {float((l0 - l1).abs().max()):.3e}")
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [64, 96, 128, 256])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", EDGE_N)
@@ -74,7 +74,7 @@ def test_fwd_small_and_large_grids(N, causal, dtype, D):
     _both_kernels(f"grid_n{N}_d{D}", seed, N, N, dtype, causal, forward, D)
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("nq,nk", [(5, 300), (100, 1000), (257, 4096), (512, 8192)])
 def test_split_one_range_small_and_large_grids(nq, nk, causal, D):
@@ -106,7 +106,7 @@ def test_small_grid_unusual_scales(scale):
     gu.assert_within(err, "bf16", f"{w.name} scale={scale}")
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [64, 96, 128, 256])
 @pytest.mark.parametrize("B,H", [(3, 5), (2, 40)])
 def test_small_grid_every_output_written(B, H, D):
     """Outputs prefilled with NaN: every row of every head of a ragged small
