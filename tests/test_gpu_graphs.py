@@ -45,11 +45,15 @@ def _check_replays(run, outs):
         torch.cuda.synchronize()
 
 
-def test_graph_fa_fwd():
-    w = fi.Workload("graph_fwd", 1100, 1, 4, 777, 128, "bf16", True)
+@pytest.mark.parametrize("B,H", [(1, 4), (2, 40)], ids=["small_grid", "large_grid"])
+def test_graph_fa_fwd(B, H):
+    """fa_fwd in a graph: a grid that takes the 64-row small-grid kernel (B=1
+    H=4: 28 blocks of 128 rows) and one that takes the 128-row kernel (B=2
+    H=40: 560 blocks)."""
+    w = fi.Workload(f"graph_fwd_b{B}_h{H}", 1100, B, H, 777, 128, "bf16", True)
     q, k, v = gu.workload_tensors(w)
     o = torch.empty_like(q)
-    lse = torch.empty((1, 4, 777), device="cuda")
+    lse = torch.empty((B, H, 777), device="cuda")
     _check_replays(lambda: fa.attention_forward(q, k, v, causal=True, scale=w.scale, out=o, lse=lse), [o, lse])
 
 
