@@ -92,10 +92,10 @@ int cu_count() {
 
 // Whether a one-range 16-bit launch goes to the 16-row-wave kernel: when its
 // 128-row grid (a, made for 128 rows) holds at most one workgroup per compute
-// unit.  There a wave's time per tile sets the
-// kernel's, and halving a wave's rows per tile wins; on larger grids the
-// 128-row kernel's larger MFMA tiles read LDS half as often per query and win.
-bool use_rows16(int dtype, int D, const FwdArgs& a) {
+// unit.  There a wave's time per tile sets the kernel's, and halving a wave's
+// rows per tile wins; on larger grids the 128-row kernel's larger MFMA tiles
+// read LDS half as often per query and win.
+bool use_rows16(int dtype, const FwdArgs& a) {
   return dtype != FA_DTYPE_F32 && a.n_split == 1 && a.n_blocks <= cu_count();
 }
 
@@ -114,13 +114,13 @@ hipError_t launch_rows16(int dtype, bool causal, FwdArgs a, hipStream_t s) {
 }
 
 // One-range 16-bit launch: on small grids the 16-row-wave kernel, else the
-// 128-row kernel.  At D = 64, 96 and 128: two waves per slice when the 64-row
-// grid fits one workgroup per CU (8 waves, one workgroup per CU), one wave per
-// slice when it needs two per CU.  At D = 256
-// the 128 KB of tiles allow one workgroup per CU in either form, and two waves
-// per slice (two per SIMD) are always the faster.
+// 128-row kernel.  At D = 64, 96 and 128 the small-grid kernel runs two waves
+// per slice when its 64-row grid fits one workgroup per CU (8 waves, one
+// workgroup per CU) and one wave per slice when it needs two per CU.  At
+// D = 256 its 128 KB of tiles allow one workgroup per CU either way, and two
+// waves per slice (two per SIMD) are always the faster.
 hipError_t launch_h16_one(int dtype, int D, bool causal, const FwdArgs& a, hipStream_t s) {
-  if (use_rows16(dtype, D, a)) {
+  if (use_rows16(dtype, a)) {
     if (D == 256) return launch_rows16<256, 2>(dtype, causal, a, s);
     const bool two = a.n_bh * ((a.nq + kRows16Rows - 1) / kRows16Rows) <= cu_count();
     if (D == 64) return two ? launch_rows16<64, 2>(dtype, causal, a, s) : launch_rows16<64, 1>(dtype, causal, a, s);
