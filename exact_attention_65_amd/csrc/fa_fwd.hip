@@ -94,7 +94,7 @@ int cu_count() {
 // 128-row grid (a, made for 128 rows) holds at most one workgroup per compute
 // unit.  There a wave's time per tile sets the kernel's, and halving a wave's
 // rows per tile wins; on larger grids the 128-row kernel's larger MFMA tiles
-// read LDS half as often per query and win.
+// read LDS half as often per query and win (except at D = 256, below).
 bool use_rows16(int dtype, const FwdArgs& a) {
   return dtype != FA_DTYPE_F32 && a.n_split == 1 && a.n_blocks <= cu_count();
 }
@@ -113,12 +113,25 @@ hipError_t launch_rows16(int dtype, bool causal, FwdArgs a, hipStream_t s) {
                 : launch(fa_fwd_bf16_rows16_kernel<D, false, KS>, n, a, t, s);
 }
 
-// One-range 16-bit launch: on small grids the 16-row-wave kernel, else the
-// 128-row kernel.  At D = 64, 96 and 128 the small-grid kernel runs two waves
-// per slice when its 64-row grid fits one workgroup per CU (8 waves, one
-// workgroup per CU) and one wave per slice when it needs two per CU.  At
-// D = 256 its 128 KB of tiles allow one workgroup per CU either way, and two
-// waves per slice (two per SIMD) are always the faster.
+// The 16-row-wave kernel in 128-row workgroups of 8 waves, for D = 256 on
+// grids larger than the small-grid form's; the arguments are the 128-row
+// kernel's (same blocks and order).
+hipError_t launch_rows16x8(int dtype, bool causal, const FwdArgs& a, hipStream_t s) {
+  const int t = 512, n = a.n_blocks;
+  if (dtype == FA_DTYPE_F16)
+    return causal ? launch(fa_fwd_f16_rows16x8_kernel<256, true>, n, a, t, s)
+                  : launch(fa_fwd_f16_rows16x8_kernel<256, false>, n, a, t, s);
+  return causal ? launch(fa_fwd_bf16_rows16x8_kernel<256, true>, n, a, t, s)
+                : launch(fa_fwd_bf16_rows16x8_kernel<256, false>, n, a, t, s);
+}
+
+// One-range 16-bit launch: on small grids the 16-row-wave kernel in 64-row
+// workgroups; on larger ones the 128-row kernel, or at D = 256 the 16-row-wave
+// kernel in 128-row workgroups.  At D = 64, 96 and 128 the small-grid kernel
+// runs two waves per slice when its 64-row grid fits one workgroup per CU
+// (8 waves, one workgroup per CU) and one wave per slice when it needs two
+// per CU.  At D = 256 its 128 KB of tiles allow one workgroup per CU either
+// way, and two waves per slice (two per SIMD) are always the faster.
 hipError_t launch_h16_one(int dtype, int D, bool causal, const FwdArgs& a, hipStream_t s) {
   if (use_rows16(dtype, a)) {
     if (D == 256) return launch_rows16<256, 2>(dtype, causal, a, s);
@@ -127,6 +140,7 @@ hipError_t launch_h16_one(int dtype, int D, bool causal, const FwdArgs& a, hipSt
     if (D == 96) return two ? launch_rows16<96, 2>(dtype, causal, a, s) : launch_rows16<96, 1>(dtype, causal, a, s);
     return two ? launch_rows16<128, 2>(dtype, causal, a, s) : launch_rows16<128, 1>(dtype, causal, a, s);
   }
+  if (D == 256) return launch_rows16x8(dtype, causal, a, s);
   return launch_h16<false>(dtype, D, causal, a, s);
 }
 

@@ -1,6 +1,7 @@
-// Exact attention forward for small grids: 16 query rows per wave on the
-// 16x16x32 MFMA (bf16 or fp16 inputs, D = 64, 96, 128 or 256, one key range;
-// D = 96 in LDS rows of 128 columns, as in the 128-row kernel).
+// Exact attention forward with 16 query rows per wave on the 16x16x32 MFMA
+// (bf16 or fp16 inputs, one key range): for small grids at D = 64, 96, 128 and
+// 256 (D = 96 in LDS rows of 128 columns, as in the 128-row kernel), and for
+// every larger grid at D = 256.
 //
 // The method is the 128-row kernel's: the tiled loop of "Flash Attention"
 // (wiki.ai-engineering.at, section "Tiling Algorithm") with the online
@@ -18,7 +19,15 @@
 // sets); the per-wave work halves again, until the K and V bytes each
 // workgroup must fetch per tile (32 KB) bound the tile time instead.  On large
 // grids the 128-row kernel stays faster (its 32x32 tiles use each K and V
-// byte fetched into a CU for twice as many queries).  The arithmetic is the
+// byte fetched into a CU for twice as many queries), except at D = 256.
+//
+// At D = 256 the 128-row kernel's 128 KB of tiles and 32-row waves leave one
+// workgroup of 4 waves per CU, one wave alone on each SIMD.  With SL = 8
+// slices of 16 rows a workgroup holds the same 128 rows and tiles in 8 waves
+// (252 VGPRs each), two per SIMD, which fill each other's gaps; each K and V
+// byte fetched into the CU still serves 128 queries.  The 16x16 tiles read
+// each LDS operand byte for 16 queries instead of 32, which at D = 128 costs
+// more than the second wave per SIMD gains there.  The arithmetic is the
 // 128-row kernel's: scores, the lazy reference with the same headroom, P
 // rounded to the input type, the sum of the rounded P on the matrix core and
 // the fp32 sum for the LSE.
@@ -40,7 +49,7 @@
 
 namespace fa {
 
-constexpr int kRows16Rows = 64;  // query rows per workgroup: 4 slices of 16
+constexpr int kRows16Rows = 64;  // query rows per workgroup of the small-grid form: 4 slices of 16
 
 namespace rows16 {
 // Key of row t of score block b of a 64-key tile.
@@ -92,11 +101,13 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 }  // namespace rows16
 
-// KS waves per 16-row slice: with KS = 2, wave (slice, half) takes keys
-// 32 half .. 32 half + 31 of every tile, so each tile's work per wave halves
-// again, and the two halves' (reference, sums, O) are merged at the end.
-template <typename E, int D, bool CAUSAL, int KS>
+// SL slices of 16 rows per workgroup (4: 64 rows, or 8: 128 rows) and KS
+// waves per slice: with KS = 2, wave (slice, half) takes keys 32 half ..
+// 32 half + 31 of every tile, so each tile's work per wave halves again, and
+// the two halves' (reference, sums, O) are merged at the end.
+template <typename E, int D, bool CAUSAL, int KS, int SL>
 __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
+  constexpr int ROWS = 16 * SL;                // query rows per workgroup
   typedef typename E::vec8 vec8;
   constexpr int BN = 64;                       // keys per tile
   constexpr int DP = D == 96 ? 128 : D;        // LDS row width (columns)
@@ -105,8 +116,8 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   constexpr int CPR = DP / 8;                  // 16-byte chunks per LDS row
   constexpr int RPB = 64 / CPR;                // rows per wave-wide load
   constexpr int TILE16 = BN * CPR;             // chunks per tile
-  constexpr int NT = 256 * KS;                 // threads
-  constexpr int NLD = TILE16 / 64 / (4 * KS);  // wave-wide loads per wave per tile
+  constexpr int NT = 64 * SL * KS;             // threads
+  constexpr int NLD = TILE16 / 64 / (SL * KS);  // wave-wide loads per wave per tile
   constexpr int NKS = DP / 32;                 // 32-deep steps of the score contraction
   constexpr int NKB = BN / 16 / KS;            // 16-key score blocks per wave and tile
   constexpr int NSA = NKS * NKB;               // score MFMAs per wave and tile (phase A slots)
@@ -115,6 +126,8 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   constexpr int NSB = NDB * NST;               // value MFMAs per wave and tile (phase B slots)
   constexpr int PFA = 3, PFB = 4;              // fragment reads in flight
   static_assert(KS == 1 || KS == 2, "one or two waves per slice");
+  static_assert(SL == 4 || (SL == 8 && KS == 1), "slices");
+  static_assert(NLD >= 1, "tile loads");
   static_assert(D == 64 || D == 96 || D == 128 || D == 256, "head dimensions");
   static_assert(NKS >= 2 && NKB >= 2 && NSB > NKB, "slot layout");
 
@@ -122,20 +135,22 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int slice = wave & 3, half = wave >> 2;  // half = 0 when KS = 1
+  const int slice = wave % SL, half = wave / SL;  // half = 0 when KS = 1
   const int kb0 = half * NKB, st0 = half * NST;  // this wave's first score block and key step
   const int g = lane >> 4, t16 = lane & 15;
   const int NQ = a.nq, NK = a.nk;
   const int OFF = CAUSAL ? NK - NQ : 0;
-  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_bh, a.n_qblk, CAUSAL, true);
+  // (the causal pairing of long and short blocks on a CU is for two
+  // workgroups per CU, which the 128 KB of tiles at D = 256 do not allow)
+  const HeadItem wi = head_item(xcd_remap(blockIdx.x, a.n_blocks), a.n_bh, a.n_qblk, CAUSAL, D != 256);
   const int bh = wi.bh;
   const int qb = CAUSAL ? a.n_qblk - 1 - wi.idx : wi.idx;  // causal: longest query blocks first
-  const int q0 = qb * kRows16Rows;
+  const int q0 = qb * ROWS;
   const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + (size_t)bh * NQ * D;
   const uint16_t* __restrict__ Kg = (const uint16_t*)a.k + (size_t)bh * NK * D;
   const uint16_t* __restrict__ Vg = (const uint16_t*)a.v + (size_t)bh * NK * D;
 
-  const int kv_end = CAUSAL ? min(NK, q0 + kRows16Rows + OFF) : NK;
+  const int kv_end = CAUSAL ? min(NK, q0 + ROWS + OFF) : NK;
   const int n_tiles = (kv_end + BN - 1) / BN;
   const int qrow = q0 + slice * 16 + t16;  // this lane's query row
   const int wave_q0 = q0 + slice * 16;
@@ -469,14 +484,24 @@ __device__ __forceinline__ void fwd_rows16_body(const FwdArgs& a) {
   }
 }
 
-// 256 KS threads; two workgroups per CU with one wave per slice, one with two
+// 64-row workgroups of 256 KS threads; two workgroups per CU with one wave
+// per slice, one with two
 template <int D, bool CAUSAL, int KS>
 __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void fa_fwd_bf16_rows16_kernel(FwdArgs a) {
-  fwd_rows16_body<BF16, D, CAUSAL, KS>(a);
+  fwd_rows16_body<BF16, D, CAUSAL, KS, 4>(a);
 }
 template <int D, bool CAUSAL, int KS>
 __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void fa_fwd_f16_rows16_kernel(FwdArgs a) {
-  fwd_rows16_body<F16, D, CAUSAL, KS>(a);
+  fwd_rows16_body<F16, D, CAUSAL, KS, 4>(a);
+}
+// 128-row workgroups of 8 waves (D = 256), one per CU
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fa_fwd_bf16_rows16x8_kernel(FwdArgs a) {
+  fwd_rows16_body<BF16, D, CAUSAL, 1, 8>(a);
+}
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fa_fwd_f16_rows16x8_kernel(FwdArgs a) {
+  fwd_rows16_body<F16, D, CAUSAL, 1, 8>(a);
 }
 
 }  // namespace fa

@@ -112,8 +112,10 @@ fa_status fa_fwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal,
  * grid of at most one such workgroup per compute unit
  * (B * H * ceil(N / 128) <= the device's CU count) runs instead on a kernel of
  * 64 rows per workgroup and 16 per wave, whose waves finish each key tile in
- * about half the time.  Both give the same results up to the order of the
- * fp32 additions behind the LSE.
+ * about half the time, and at D = 256 a larger grid runs on that kernel in
+ * 128-row workgroups of 8 waves (two per SIMD instead of one).  All give the
+ * same results up to the order of the fp32 additions (the sums that
+ * normalise O and give the LSE).
  *
  * The caller owns every buffer; the call allocates nothing (workspace 0).
  * Arguments are validated on the host before anything is enqueued and an

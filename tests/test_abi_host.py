@@ -218,9 +218,9 @@ def test_every_kernel_stub_is_defined():
     # bf16 and fp16: D (64, 96, 128, 256) x causal x split; fp32: D x causal; merge: D x (bf16, fp16);
     # backward: (bf16, fp16) x 3 kernels (dq, dk/dv, both in one grid) x D (64, 96, 128) x causal and the
     # Delta kernel (bf16, fp16) x D; fp8: D (64, 128, 256) x causal; one-query-row: (bf16, fp16) x
-    # D (64, 128, 256); 64-row kernel for small grids: (bf16, fp16) x causal x (D 64, 96 and 128 with one
-    # or two waves per slice, D 256 with two)
-    assert len(kernels) == 32 + 4 + 8 + 36 + 6 + 6 + 6 + 28, kernels
+    # D (64, 128, 256); 16-row-wave kernel: (bf16, fp16) x causal x (64-row form for small grids: D 64, 96
+    # and 128 with one or two waves per slice, D 256 with two; 128-row form: D 256)
+    assert len(kernels) == 32 + 4 + 8 + 36 + 6 + 6 + 6 + 28 + 4, kernels
 
 
 # ---------------------------------------------------------------- fa_fwd_split

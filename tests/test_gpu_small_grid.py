@@ -6,10 +6,11 @@ workgroup per compute unit (B * H * ceil(Nq / 128) <= CU count) on a kernel
 with 64 rows per workgroup in slices of 16: at D = 64, 96 and 128 with two waves
 per slice when its 64-row grid fits one workgroup per CU and one wave per
 slice otherwise, at D = 256 always with two.  Larger grids run the 128-row
-kernel.  Each case runs the same heads with H = 2 (two waves per slice), with
+kernel, or at D = 256 the same 16-row-wave kernel in 128-row workgroups of
+8 waves.  Each case runs the same heads with H = 2 (two waves per slice), with
 the smallest H for one wave per slice (when the shape has one; at D = 256 a
 second grid of two waves per slice) and with the smallest H for the 128-row
-kernel on this device.  A head's inputs depend only on its (b, h) and the
+workgroups on this device.  A head's inputs depend only on its (b, h) and the
 seed, so heads 0 and 1 are the same in every run; each run is checked against
 the oracle on heads 0, 1 and the last, every row and column.
 """
@@ -125,3 +126,27 @@ def test_small_grid_every_output_written(B, H, D):
         outs.append((o.clone(), lse.clone()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
     gu.compare_heads(w, outs[0][0], outs[0][1], [(0, 0), (1, 2), (B - 1, H - 1)], what=w.name)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d256_large_grid_every_output_written(causal, dtype):
+    """D = 256 on a grid of more 128-row blocks than CUs (the 8-wave form):
+    N = 333 (3 blocks per head, the last of 77 rows), outputs prefilled with
+    NaN, every output written, two calls give the same bits, and heads at both
+    ends of the grid match the oracle."""
+    B, H = 3, _cus() // 9 + 1
+    assert B * H * 3 > _cus()
+    w = fi.Workload(f"grid_d256_{dtype}_b{B}_h{H}_n333", 1170 + causal, B, H, 333, 256, dtype, causal)
+    gu.log(f"[gpu] {w.name}: causal={causal}")
+    q, k, v = gu.workload_tensors(w)
+    outs = []
+    for _ in range(2):
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+        fa.attention_forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+        outs.append((o.clone(), lse.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    gu.compare_heads(w, outs[0][0], outs[0][1], [(0, 0), (1, H // 2), (B - 1, H - 1)], what=w.name)

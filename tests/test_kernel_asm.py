@@ -59,13 +59,14 @@ def test_bf16_kernels_present(asm):
     names = [n for n, _ in _kernels(asm)]
     assert sum("fwd_bf16" in n and "rows16" not in n for n in names) == 16, names
     assert sum("fwd_f16" in n and "rows16" not in n for n in names) == 16, names
-    assert sum("rows16" in n for n in names) == 28, names
+    assert sum("rows16_kernel" in n for n in names) == 28, names
+    assert sum("rows16x8_kernel" in n for n in names) == 4, names
     assert sum("combine" in n for n in names) == 8, names
 
 
 def test_every_tile_barrier_drains_vmcnt(asm):
     kernels = [(n, b) for n, b in _kernels(asm) if "fwd_bf16" in n or "fwd_f16" in n]
-    assert len(kernels) == 60
+    assert len(kernels) == 64
     for name, body in kernels:
         waits = _barrier_waits(body)
         assert waits, f"{name}: no barrier after a tile load"
