@@ -6,7 +6,9 @@
 // which reads both.  When the dq and dk/dv workgroups together fit one per
 // compute unit, the two walks over the tiles can run side by side instead:
 // fa_bwd_delta_kernel writes Delta and -LSE log2(e), then fa_bwd_fused_kernel
-// runs the dk/dv and dq workgroups in one grid.
+// runs the dk/dv and dq workgroups in one grid.  At D = 256 the dk/dv work
+// runs on fa_bwd_dkdv16_kernel (16 keys per wave, 64 per workgroup), always
+// after the dq kernel (the two bodies' tiles together exceed the LDS).
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -46,12 +48,17 @@ hipError_t launch_fused(bool causal, const BwdArgs& a, hipStream_t s) {
 
 template <typename E, int D>
 hipError_t launch_bwd_d(bool causal, const BwdArgs& a, hipStream_t s) {
-  if (fuse_bwd(a)) return launch_fused<E, D>(causal, a, s);
+  if constexpr (D != 256)
+    if (fuse_bwd(a)) return launch_fused<E, D>(causal, a, s);
   const hipError_t e = causal ? launch(fa_bwd_dq_kernel<E, D, true>, a, a.n_qblocks, s)
                               : launch(fa_bwd_dq_kernel<E, D, false>, a, a.n_qblocks, s);
   if (e != hipSuccess) return e;
-  return causal ? launch(fa_bwd_dkdv_kernel<E, D, true>, a, a.n_kblocks, s)
-                : launch(fa_bwd_dkdv_kernel<E, D, false>, a, a.n_kblocks, s);
+  if constexpr (D == 256)
+    return causal ? launch(fa_bwd_dkdv16_kernel<E, D, true>, a, a.n_kblocks, s)
+                  : launch(fa_bwd_dkdv16_kernel<E, D, false>, a, a.n_kblocks, s);
+  else
+    return causal ? launch(fa_bwd_dkdv_kernel<E, D, true>, a, a.n_kblocks, s)
+                  : launch(fa_bwd_dkdv_kernel<E, D, false>, a, a.n_kblocks, s);
 }
 
 template <typename E>
@@ -60,6 +67,7 @@ hipError_t launch_bwd_typed(int D, bool causal, BwdArgs a, float scale, hipStrea
   // bit of both 16-bit types is bit 15)
   a.flip = std::signbit(scale) && scale != 0.0f ? 0x80008000u : 0u;
   if (D == 128) return launch_bwd_d<E, 128>(causal, a, s);
+  if (D == 256) return launch_bwd_d<E, 256>(causal, a, s);
   if (D == 96) return launch_bwd_d<E, 96>(causal, a, s);
   return launch_bwd_d<E, 64>(causal, a, s);
 }
@@ -94,7 +102,8 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   a.nq = (int)Nq;
   a.nk = (int)Nk;
   a.n_qblk = (int)((Nq + kBwdRows - 1) / kBwdRows);
-  a.n_kblk = (int)((Nk + kBwdRows - 1) / kBwdRows);
+  const int64_t kpb = bwd_keys_per_block(D);  // keys per dk/dv workgroup
+  a.n_kblk = (int)((Nk + kpb - 1) / kpb);
   a.n_qblocks = (int)(B * H * a.n_qblk);
   a.n_kblocks = (int)(B * H * a.n_kblk);
   const float c = std::fabs(scale) * 1.44269504088896340736f;

@@ -13,9 +13,11 @@
 //                       dQ^T += K^T dS^T; it also writes Delta for its rows;
 //   fa_bwd_dkdv_kernel  one workgroup per 128 keys, Q and dO tiles streamed:
 //                       S = Q K^T, dP = dO V^T, then dV^T += dO^T P and
-//                       dK^T += Q^T dS.
-// Every contraction runs on the 32x32x16 MFMA of the input type (bf16 or fp16)
-// with fp32 accumulators; P and dS are rounded to that type as MFMA operands,
+//                       dK^T += Q^T dS (at D = 256 fa_bwd_dkdv16_kernel, one
+//                       workgroup per 64 keys, the same products on the
+//                       16x16x32 MFMA).
+// Every other contraction runs on the 32x32x16 MFMA of the input type (bf16
+// or fp16) with fp32 accumulators; P and dS are rounded to that type as MFMA operands,
 // the outputs once.  The kernels are templates over the element type E (BF16 or
 // F16, the forward's element-type structs).
 #pragma once
@@ -38,7 +40,7 @@ struct BwdArgs {
   float* nlse2;      // [B*H*Nq] workspace: -LSE log2(e) per query row
   int nq, nk;        // queries and keys per (b, h); causal: query i is position i + nk - nq
   int n_qblk;        // 128-row query blocks per (b, h)
-  int n_kblk;        // 128-key blocks per (b, h)
+  int n_kblk;        // dk/dv key blocks per (b, h): 128 keys, 64 at D = 256
   int n_qblocks;     // dq workgroups: B * H * n_qblk
   int n_kblocks;     // dk/dv workgroups: B * H * n_kblk
   float c;           // |scale| * log2(e), at least FLT_MIN
@@ -59,10 +61,12 @@ namespace bwd {
 // that share a bank line and sends each aligned group of 4 rows to 4
 // different groups of 4 chunks:
 //   D = 128 (one row per line):  row = 4a + b  ->  4b + a  (a, b < 4);
-//   D = 64  (two rows per line): the 3 bits of (row >> 1) & 7 reversed.
+//   D = 64  (two rows per line): the 3 bits of (row >> 1) & 7 reversed;
+//   D = 256 (two lines per row): as D = 128, since every row starts on the
+//   same bank and the XOR keeps a chunk within its 256-byte line.
 template <int D>
 __device__ __forceinline__ int bswz(int row) {
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
   else {
     const int u = (row >> 1) & 7;
     return ((u & 1) << 2) | (u & 2) | (u >> 2);
@@ -301,9 +305,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
   auto compute = [&](const u32x4* Kt, const u32x4* Vt, int j) __attribute__((always_inline)) {
     constexpr int NSS = 2 * NKB * NKK, NSG = NDB * NCC, PF = 4;
     // a block's 16 elementwise steps spread over half a phase's slots: slot
-    // k of that half takes steps [16k / H, 16(k+1) / H), H = slots / 2
+    // k of that half takes steps [16k / H, 16(k+1) / H), H = slots / 2 (at
+    // D = 256, 32 slots: one step every second slot)
     constexpr int HS = NSS / 2, HG = NSG / 2;
-    static_assert(HS <= 16 && HG <= 16 && NKB == 2, "slot layout");
+    static_assert(HS <= 32 && HG <= 16 && NKB == 2, "slot layout");
     const int kv0 = j * BN;
     const bool masked = kv0 + BN > NK || (CAUSAL && kv0 + BN - 1 > wave_q0 + OFF);
     f32x16 s[NKB], dp[NKB];
@@ -382,8 +387,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk) {
   if (qrow < N) bwd::store_rows<E>((uint16_t*)a.dq + head + (size_t)qrow * D, dqa, h, a.scale);
 }
 
+// two workgroups per CU; at D = 256 (Q, dO and dQ of 32 rows take 256
+// registers per lane) one, with 512 registers per lane over VGPRs and AGPRs
 template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads, D == 256 ? 1 : 2) void fa_bwd_dq_kernel(BwdArgs a) {
   bwd_dq_body<E, D, CAUSAL, true>(a, blockIdx.x);
 }
 
@@ -614,6 +621,301 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk) {
 template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   bwd_dkdv_body<E, D, CAUSAL>(a, blockIdx.x);
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV at D = 256: 16 keys per wave on the 16x16x32 MFMA, 4 waves (64
+// keys) per workgroup.  With 32 keys per wave the body above would hold
+// 256 registers of dK and dV accumulators and 128 of K and V per lane, more
+// than a wave can have; with 16 keys it holds half of each (about 300 in all,
+// one wave per SIMD).  Q and dO tiles of 64 queries and their -LSE log2(e)
+// and Delta stream through double-buffered LDS as there.  Per tile and wave:
+//   * S = Q K^T and dP = dO V^T: 4 blocks of 16 queries x D/32 steps of 32 d
+//     (A = Q or dO rows from LDS, B = this lane's key from registers).  Row t
+//     of block b is query 32 (b >> 1) + 8 (t >> 2) + 4 (b & 1) + (t & 3), so
+//     lane l's results of blocks 2s and 2s + 1 are queries 32s + 8 (l / 16)
+//     + 0..7 of its key l % 16: the B fragment (k block l / 16) of gradient
+//     step s, with no data movement;
+//   * P = exp2(c s - LSE log2 e) and dS = P (dP - Delta), rounded to the
+//     16-bit type;
+//   * dV^T += dO^T P and dK^T += Q^T dS: D/16 blocks of 16 d x 2 steps of 32
+//     queries, dO^T and Q^T by transposed reads (two ds_read_b64_tr_b16 per
+//     fragment, the forward's V^T pattern).
+// Each tile is read both ways, so one chunk swizzle serves both patterns:
+// (r3 ^ r4) | r0 << 1 | r1 << 2 | r3 << 3, chosen with a bank model over every
+// lane of both (conflict-free for 8 and 16 lanes a pass of the 16-byte reads,
+// 16 and 32 of the 8-byte ones; 512-byte rows all start on the same bank,
+// and the XOR keeps a chunk within its 256-byte line).  It reads only row
+// bits 0, 1, 3 and 4, which are constant over a lane's reads.
+namespace bwd16 {
+__device__ __forceinline__ int query_of(int b, int t) { return 32 * (b >> 1) + 8 * (t >> 2) + 4 * (b & 1) + (t & 3); }
+__device__ __forceinline__ int swz(int row) {
+  const int r0 = row & 1, r1 = (row >> 1) & 1, r3 = (row >> 3) & 1, r4 = (row >> 4) & 1;
+  return (r3 ^ r4) | (r0 << 1) | (r1 << 2) | (r3 << 3);
+}
+}  // namespace bwd16
+
+template <typename E, int D, bool CAUSAL>
+__device__ __forceinline__ void bwd_dkdv16_body(const BwdArgs& a, int blk) {
+  typedef typename E::vec8 vec8;
+  constexpr int NW = kBwdThreads / 64;    // waves, 16 keys each
+  constexpr int KPB = 16 * NW;            // keys per workgroup
+  constexpr int BQ = 64, RB = D * 2, CPR = D / 8, RPB = 64 / CPR, TILE16 = BQ * CPR;
+  constexpr int NLD = TILE16 / 64 / NW;   // wave-wide loads per wave and tensor
+  constexpr int NQB = BQ / 16;            // 16-query score blocks per tile
+  constexpr int NKS = D / 32;             // 32-deep d steps of S and dP
+  constexpr int NDB = D / 16;             // 16-wide d blocks of dK^T and dV^T
+  constexpr int NST = BQ / 32;            // 32-query steps of the gradient products
+  constexpr int NSS = 2 * NQB * NKS;      // score-phase slots (S, dP alternating)
+  constexpr int NSG = 2 * NDB * NST;      // gradient-phase slots (dV, dK alternating)
+  constexpr int HS = NSS / 2, HG = NSG / 2;
+  constexpr int PF = 4;                   // operand reads in flight
+  static_assert(D == 256 && NLD >= 1 && NQB == 4 && NST == 2, "tile layout");
+  __shared__ u32x4 qA[TILE16], qB[TILE16], gA[TILE16], gB[TILE16];
+  __shared__ f32x4 lA[BQ / 4], lB[BQ / 4], dA[BQ / 4], dB[BQ / 4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, t16 = lane & 15;
+  const int N = a.nq, NK = a.nk, OFF = CAUSAL ? NK - N : 0;
+  const HeadItem wi = head_item(xcd_remap(blk, a.n_kblocks), a.n_kblocks / a.n_kblk, a.n_kblk, CAUSAL, false);
+  const int bh = wi.bh;
+  const int k0 = wi.idx * KPB;  // causal: the first key blocks see the most queries
+  const size_t head = (size_t)bh * N * D, headk = (size_t)bh * NK * D;
+  const uint16_t* Qg = (const uint16_t*)a.q + head;
+  const uint16_t* Kg = (const uint16_t*)a.k + headk;
+  const uint16_t* Vg = (const uint16_t*)a.v + headk;
+  const uint16_t* dOg = (const uint16_t*)a.dout + head;
+  const float* Lg = a.nlse2 + (size_t)bh * N;
+  const float* Dg = a.delta + (size_t)bh * N;
+
+  const int key = k0 + wave * 16 + t16;  // this lane's key
+  const int wave_k0 = k0 + wave * 16;
+  const int n_qt = (N + BQ - 1) / BQ;
+  const int t_first = CAUSAL ? max(0, k0 - OFF) / BQ : 0;      // first query tile seeing key k0
+  const int t_wave = CAUSAL ? max(0, wave_k0 - OFF) / BQ : 0;  // first one seeing this wave's first key
+  const bool active = wave_k0 < NK;
+
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < TILE16; i += kBwdThreads) qA[i] = qB[i] = gA[i] = gB[i] = z;
+  }
+
+  // this lane's key as B fragments of the score products: K[key][32 ks + 8 g
+  // .. +7] (signs flipped for a negative scale) and V likewise; zero past NK
+  vec8 kreg[NKS], vreg[NKS];
+  {
+    const u32x4 fl = {a.flip, a.flip, a.flip, a.flip};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (key < NK) {
+        x = *(const u32x4*)(Kg + (size_t)key * D + 32 * ks + 8 * g) ^ fl;
+        y = *(const u32x4*)(Vg + (size_t)key * D + 32 * ks + 8 * g);
+      }
+      kreg[ks] = __builtin_bit_cast(vec8, x);
+      vreg[ks] = __builtin_bit_cast(vec8, y);
+    }
+  }
+
+  // tile DMA: LDS position cl of a row holds global chunk cl ^ swz(row)
+  uint32_t toff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int row = (wave * NLD + i) * RPB + lane / CPR;
+    toff[i] = row * RB + ((lane % CPR) ^ bwd16::swz(row)) * 16;
+  }
+  // query tile t: Q and dO rows, and the rows' -LSE log2(e) and Delta (the
+  // first wave, 4 bytes a lane); rows past N are outside the descriptors and
+  // arrive as zeros
+  auto issue = [&](u32x4* qd, u32x4* gd, f32x4* ld, f32x4* dd, int tq) __attribute__((always_inline)) {
+    const int r0 = tq * BQ;
+    const uint32_t bytes = (uint32_t)(N - r0) * RB;
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Qg + (size_t)r0 * D), (short)0, (int)bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rg =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(dOg + (size_t)r0 * D), (short)0, (int)bytes, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      lds_load16(rq, qd + (wave * NLD + i) * 64, toff[i]);
+      lds_load16(rg, gd + (wave * NLD + i) * 64, toff[i]);
+    }
+    if (wave == 0) {
+      const uint32_t fbytes = (uint32_t)(N - r0) * 4;
+      const __amdgpu_buffer_rsrc_t rl =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Lg + r0), (short)0, (int)fbytes, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rd =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Dg + r0), (short)0, (int)fbytes, kRsrcWord3);
+      lds_load4(rl, (float*)ld, (uint32_t)lane * 4);
+      lds_load4(rd, (float*)dd, (uint32_t)lane * 4);
+    }
+  };
+
+  f32x4 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dka[db][i] = dva[db][i] = 0.0f;
+
+  // row read of block b, step ks: row query_of(b, t16), chunk 4 ks + g; the
+  // swizzle of query_of(b, t16) is that of query_of(0, t16), so the address is
+  // one per-lane base XOR (ks << 6) plus the block's row offset
+  const uint32_t raddr0 = [&] {
+    const int row = bwd16::query_of(0, t16);
+    return (uint32_t)(row * RB + ((g ^ bwd16::swz(row)) * 16));
+  }();
+  // transposed read of d block db, step st: in 16-lane group g, lane 4r + q
+  // addresses row 32 st + 8 g + r (and + 4), columns 16 db + 4q .. +3; chunk
+  // (2 db + q / 2) ^ swz(row) is the db = 0 one XOR 2 db
+  const uint32_t taddr0 = [&] {
+    const int r = t16 >> 2, q = t16 & 3;
+    const int row = 8 * g + r;
+    return (uint32_t)(row * RB + (((q >> 1) ^ bwd16::swz(row)) * 16) + (q & 1) * 8);
+  }();
+  // operand of score slot f: block f / (2 NKS), step (f / 2) % NKS of Q (even
+  // f: S) or dO (odd f: dP); of gradient slot f: step f / (2 NDB), d block
+  // (f / 2) % NDB of dO^T (even f: dV) or Q^T (odd f: dK)
+  auto sfrag = [&](const u32x4* Qt, const u32x4* Gt, int f) __attribute__((always_inline)) {
+    const int b = f / (2 * NKS), ks = (f / 2) % NKS;
+    const char* t = (const char*)((f & 1) ? Gt : Qt);
+    return *(const u32x4*)(t + ((raddr0 ^ (uint32_t)(ks << 6)) + (32 * (b >> 1) + 4 * (b & 1)) * RB));
+  };
+  auto gfrag = [&](const u32x4* Qt, const u32x4* Gt, int f) __attribute__((always_inline)) {
+    const int st = f / (2 * NDB), db = (f / 2) % NDB;
+    const char* p = (const char*)((f & 1) ? Qt : Gt) + (taddr0 ^ (uint32_t)(db << 5)) + 32 * st * RB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+    const i16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 4 * RB));
+    return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  auto compute = [&](const u32x4* Qt, const u32x4* Gt, const f32x4* Lt, const f32x4* Dt, int tq)
+      __attribute__((always_inline)) {
+    // tiles with a query past N or (causal) before one of the wave's keys
+    const bool masked = (CAUSAL && tq * BQ + OFF < wave_k0 + 15) || tq * BQ + BQ > N;
+    const float c = a.c;
+    f32x4 s[NQB], dp[NQB];
+    vec8 pf[NST], dsf[NST];
+    uint32_t pw[NQB][2], dw[NQB][2];
+    // element i of block b is query tq BQ + 32 (b >> 1) + 8 g + 4 (b & 1) + i of
+    // this lane's key; the rows' -LSE log2(e) and Delta, read before the tile's
+    // first MFMA so that no wait for them drains the operand reads in flight
+    f32x4 nl[NQB], dl[NQB];
+#pragma unroll
+    for (int b = 0; b < NQB; ++b) {
+      const int q4 = 8 * (b >> 1) + 2 * g + (b & 1);
+      nl[b] = Lt[q4];
+      dl[b] = Dt[q4];
+    }
+    auto mask_block = [&](int b) __attribute__((always_inline)) {
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int qg = tq * BQ + 32 * (b >> 1) + 8 * g + 4 * (b & 1) + i;
+          if (qg >= N || (CAUSAL && qg + OFF < key)) s[b][i] = neg_inf();
+        }
+      }
+    };
+    // element e: block e / 4, entry e % 4; a block's four 16-bit P and dS
+    // values once its last entry is done, and gradient step s's fragments
+    // once blocks 2s and 2s + 1 are
+    auto elem = [&](int e) __attribute__((always_inline)) {
+      const int b = e >> 2, i = e & 3;
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][i], c, nl[b][i]));
+      float ds = p * (dp[b][i] - dl[b][i]);
+      float pp = p;
+      pin(pp);
+      pin(ds);
+      s[b][i] = pp;
+      dp[b][i] = ds;
+      if (i == 3) {
+        pw[b][0] = E::pack(s[b][0], s[b][1]);
+        pw[b][1] = E::pack(s[b][2], s[b][3]);
+        dw[b][0] = E::pack(dp[b][0], dp[b][1]);
+        dw[b][1] = E::pack(dp[b][2], dp[b][3]);
+        if (b & 1) {
+          const int st = b >> 1;
+          pf[st] = __builtin_bit_cast(vec8, u32x4{pw[b - 1][0], pw[b - 1][1], pw[b][0], pw[b][1]});
+          dsf[st] = __builtin_bit_cast(vec8, u32x4{dw[b - 1][0], dw[b - 1][1], dw[b][0], dw[b][1]});
+        }
+      }
+    };
+
+    u32x4 sf[NSS], gf[NSG];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) sf[k] = sfrag(Qt, Gt, k);
+    // score phase; blocks 0 and 1's elements beside blocks 2 and 3's MFMAs
+#pragma unroll
+    for (int k = 0; k < NSS; ++k) {
+      if (k + PF < NSS) sf[k + PF] = sfrag(Qt, Gt, k + PF);
+      else gf[k + PF - NSS] = gfrag(Qt, Gt, k + PF - NSS);
+      const int b = k / (2 * NKS), ks = (k / 2) % NKS;
+      const f32x4 z = {};
+      if (k & 1)
+        dp[b] = E::mfma16(__builtin_bit_cast(vec8, sf[k]), vreg[ks], ks == 0 ? z : dp[b]);
+      else
+        s[b] = E::mfma16(__builtin_bit_cast(vec8, sf[k]), kreg[ks], ks == 0 ? z : s[b]);
+      if (k == HS) {
+        mask_block(0);
+        mask_block(1);
+      }
+      if (k >= HS)
+#pragma unroll
+        for (int e = (k - HS) * 8 / HS; e < (k - HS + 1) * 8 / HS; ++e) elem(e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // gradient phase; blocks 2 and 3's elements beside step 0's MFMAs
+#pragma unroll
+    for (int k = 0; k < NSG; ++k) {
+      if (k + PF < NSG) gf[k + PF] = gfrag(Qt, Gt, k + PF);
+      const int st = k / (2 * NDB), db = (k / 2) % NDB;
+      if (k & 1)
+        dka[db] = E::mfma16(__builtin_bit_cast(vec8, gf[k]), dsf[st], dka[db]);
+      else
+        dva[db] = E::mfma16(__builtin_bit_cast(vec8, gf[k]), pf[st], dva[db]);
+      if (k == 0) {
+        mask_block(2);
+        mask_block(3);
+      }
+      if (k < HG)
+#pragma unroll
+        for (int e = k * 8 / HG; e < (k + 1) * 8 / HG; ++e) elem(8 + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  __syncthreads();  // zeroed tiles visible before any load lands
+  if (t_first < n_qt) issue(qA, gA, lA, dA, t_first);
+  auto step = [&](int tq, const u32x4* Qt, const u32x4* Gt, const f32x4* Lt, const f32x4* Dt, u32x4* Qn,
+                  u32x4* Gn, f32x4* Ln, f32x4* Dn) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);  // see the dQ kernel
+    __syncthreads();
+    if (tq + 1 < n_qt) issue(Qn, Gn, Ln, Dn, tq + 1);
+    if (active && tq >= t_wave) compute(Qt, Gt, Lt, Dt, tq);
+  };
+  for (int tq = t_first; tq < n_qt; tq += 2) {
+    step(tq, qA, gA, lA, dA, qB, gB, lB, dB);
+    if (tq + 1 < n_qt) step(tq + 1, qB, gB, lB, dB, qA, gA, lA, dA);
+  }
+
+  // dK^T and dV^T blocks: lane l holds d = 16 db + 4 (l / 16) + i of key l % 16
+  if (key < NK) {
+    uint16_t* dkr = (uint16_t*)a.dk + headk + (size_t)key * D;
+    uint16_t* dvr = (uint16_t*)a.dv + headk + (size_t)key * D;
+    const float mul = a.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = 16 * db + 4 * g;
+      *(u32x2*)(dkr + d) = u32x2{E::pack(dka[db][0] * mul, dka[db][1] * mul),
+                                 E::pack(dka[db][2] * mul, dka[db][3] * mul)};
+      *(u32x2*)(dvr + d) = u32x2{E::pack(dva[db][0], dva[db][1]), E::pack(dva[db][2], dva[db][3])};
+    }
+  }
+}
+
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv16_kernel(BwdArgs a) {
+  bwd_dkdv16_body<E, D, CAUSAL>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------

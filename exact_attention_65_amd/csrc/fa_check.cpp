@@ -190,10 +190,11 @@ fa_status check_bwd_qk_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
   }
   // the arguments are valid; what follows decides whether the kernels support them
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
-  if (D != 64 && D != 96 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 96 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
   if (Nq * D > (int64_t)INT32_MAX || Nk * D > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
   // both grids, and their sum (the one-launch plan), within the grid limit
-  const int64_t blocks = (Nq + kRowsPerBlock - 1) / kRowsPerBlock + (Nk + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t kpb = bwd_keys_per_block(D);
+  const int64_t blocks = (Nq + kRowsPerBlock - 1) / kRowsPerBlock + (Nk + kpb - 1) / kpb;
   if (B > kMaxGrid / H || B * H > kMaxGrid / blocks) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
@@ -322,7 +323,7 @@ __attribute__((visibility("default"))) const char* fa_status_str(fa_status s) {
     case FA_ERR_ALIASING: return "FA_ERR_ALIASING: outputs and workspace must not overlap the inputs or each other";
     case FA_ERR_UNSUPPORTED:
       return "FA_ERR_UNSUPPORTED: a head dimension or dtype the entry point lacks (D in {64,96,128,256} for 16-bit "
-             "forward inputs, {64,96,128} for the backward, {64,128,256} for FP8, {64,128} for fp32), N*D >= 2^31, "
+             "forward inputs and the backward, {64,128,256} for FP8, {64,128} for fp32), N*D >= 2^31, "
              "more than 2^31-1 workgroups, or not a gfx950 device";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call failed";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace_bytes is smaller than the call needs";

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 8
+#define FA_ABI_VERSION 9
 
 /* Identical to hipStream_t.  NULL means the device's null stream. */
 typedef struct ihipStream_t* fa_stream_t;
@@ -226,7 +226,8 @@ fa_status fa_fwd_split_static(const void* q, const void* k, const void* v, void*
  * dout, dq, dk, dv, which share them), lse_bytes that of lse, and
  * workspace_bytes = B*H*N*8 (two floats per query row: sum_d dO O and
  * -LSE log2(e)).  Returns as fa_fwd_query; FA_ERR_UNSUPPORTED also for float32
- * (the backward takes bfloat16 and float16) and for D not in {64, 96, 128}.
+ * (the backward takes bfloat16 and float16) and for D not in {64, 96, 128, 256}
+ * (D = 256 since ABI version 9).
  */
 fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, fa_dtype dtype,
                        fa_sizes* out);
@@ -243,10 +244,10 @@ fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, f
  * attention в 6 раз без потери точности", section "Стадии вычисления"); the
  * formulas are the derivatives of the forward.  Two kernels on `stream`: one
  * per 128 query rows (dq, and per row Delta and the LSE in base 2 into the
- * workspace), then one per 128 keys (dk, dv); when those two grids together
- * hold at most one workgroup per compute unit, a small kernel writes Delta and
- * the LSE in base 2 and one grid then runs both kinds of workgroup.  No
- * atomics: the result is deterministic.
+ * workspace), then one per 128 keys (dk, dv; 64 keys at D = 256); when those
+ * two grids together hold at most one workgroup per compute unit (D < 256), a
+ * small kernel writes Delta and the LSE in base 2 and one grid then runs both
+ * kinds of workgroup.  No atomics: the result is deterministic.
  *
  * q, k, v, o, dout : [B, H, N, D] contiguous, element type `dtype` (bfloat16
  *                    or float16), read only (may alias).
@@ -258,7 +259,7 @@ fa_status fa_bwd_query(int64_t B, int64_t H, int64_t N, int64_t D, int causal, f
  *                    caller-owned, clobbered.
  *
  * Validation and asynchrony as in fa_fwd; FA_ERR_WORKSPACE when
- * workspace_bytes is too small.  bfloat16 or float16, D in {64, 96, 128}.
+ * workspace_bytes is too small.  bfloat16 or float16, D in {64, 96, 128, 256}.
  * Allocates nothing.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -295,7 +296,7 @@ fa_status fa_bwd_qk_query(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t 
  * workspace        : >= fa_bwd_qk_query's workspace_bytes, 16-byte aligned,
  *                    caller-owned, clobbered.
  *
- * Validation and asynchrony as in fa_bwd.  D in {64, 96, 128}.  Allocates
+ * Validation and asynchrony as in fa_bwd.  D in {64, 96, 128, 256}.  Allocates
  * nothing.
  */
 fa_status fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -75,7 +75,7 @@ def test_probe_clock_from_stamps():
 
 
 def test_version_and_strings():
-    assert fa.fa_abi_version() == 8
+    assert fa.fa_abi_version() == 9
     for st in range(10):
         s = fa.fa_status_str(st)
         assert s.startswith("FA_")
@@ -104,7 +104,8 @@ def test_query_sizes():
     assert fa.fa_fwd_query(1, 1, 256, 256, 0, fa.FA_DTYPE_F16)[0] == fa.FA_OK
     assert fa.fa_fwd_query(1, 1, 256, 256, 0, fa.FA_DTYPE_F32)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_split_query(1, 1, 16, 512, 256, 1, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
-    assert fa.fa_bwd_query(1, 1, 256, 256, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_query(1, 1, 256, 256, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
+    assert fa.fa_bwd_query(1, 1, 256, 512, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_fp8_query(1, 1, 256, 256, 0)[0] == fa.FA_OK
     assert fa.fa_fwd_fp8_query(1, 1, 256, 96, 0)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_query(1, 1, 1 << 24, 128, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
@@ -216,11 +217,12 @@ def test_every_kernel_stub_is_defined():
     assert undefined == []
     kernels = set(re.findall(r"(_ZN2fa\d+fa_\w+_kernelI\w+)", out))
     # bf16 and fp16: D (64, 96, 128, 256) x causal x split; fp32: D x causal; merge: D x (bf16, fp16);
-    # backward: (bf16, fp16) x 3 kernels (dq, dk/dv, both in one grid) x D (64, 96, 128) x causal and the
-    # Delta kernel (bf16, fp16) x D; fp8: D (64, 128, 256) x causal; one-query-row: (bf16, fp16) x
+    # backward: (bf16, fp16) x 3 kernels (dq, dk/dv, both in one grid) x D (64, 96, 128) x causal, the
+    # Delta kernel (bf16, fp16) x D and at D = 256 (bf16, fp16) x (dq, 16-key dk/dv) x causal;
+    # fp8: D (64, 128, 256) x causal; one-query-row: (bf16, fp16) x
     # D (64, 128, 256); 16-row-wave kernel: (bf16, fp16) x causal x (64-row form for small grids: D 64, 96
     # and 128 with one or two waves per slice, D 256 with two; 128-row form: D 256)
-    assert len(kernels) == 32 + 4 + 8 + 36 + 6 + 6 + 6 + 28 + 4, kernels
+    assert len(kernels) == 32 + 4 + 8 + 36 + 6 + 8 + 6 + 6 + 28 + 4, kernels
 
 
 # ---------------------------------------------------------------- fa_fwd_split
@@ -338,7 +340,7 @@ def test_bwd_query_sizes():
     assert sz.lse_bytes == 2 * 32 * 4096 * 4 and sz.workspace_bytes == 2 * sz.lse_bytes
     assert fa.fa_bwd_query(1, 1, 256, 64, 0, fa.FA_DTYPE_F32)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_bwd_query(1, 1, 256, 96, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
-    assert fa.fa_bwd_query(1, 1, 256, 256, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_query(1, 1, 256, 256, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
     assert fa.fa_bwd_query(1, 1, 256, 80, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_bwd_query(1, 1, 0, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
     assert fa.fa_bwd_query(1, 1, 256, 64, 0, 9)[0] == fa.FA_ERR_BAD_DTYPE
@@ -373,7 +375,7 @@ def bwd_call(q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, do=A + 4 * SZ, lse=A + 5
     (dict(ws=A + 8 * SZ + 16), fa.FA_ERR_ALIASING),       # workspace inside dv
     (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE),
     (dict(N=0), fa.FA_ERR_BAD_SHAPE),
-    (dict(D=256), fa.FA_ERR_UNSUPPORTED),                 # the backward takes D in {64, 96, 128}
+    (dict(D=512), fa.FA_ERR_UNSUPPORTED),                 # the backward takes D in {64, 96, 128, 256}
     (dict(D=80), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=4), fa.FA_ERR_BAD_DTYPE),
@@ -400,7 +402,8 @@ def test_bwd_qk_query_sizes():
     assert fa.fa_bwd_qk_query(1, 1, 300, 200, 64, 1, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
     assert fa.fa_bwd_qk_query(1, 1, 300, 200, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
     assert fa.fa_bwd_qk_query(1, 1, 0, 200, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_BAD_SHAPE
-    assert fa.fa_bwd_qk_query(1, 1, 100, 200, 256, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_qk_query(1, 1, 100, 200, 256, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_OK
+    assert fa.fa_bwd_qk_query(1, 1, 100, 200, 512, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_bwd_qk_query(1, 1, 100, 200, 64, 0, fa.FA_DTYPE_F32)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_bwd_qk_query(1, 1, 100, 200, 64, 0, 9)[0] == fa.FA_ERR_BAD_DTYPE
     assert fa.lib().fa_bwd_qk_query(1, 1, 100, 200, 64, 0, 1, None) == fa.FA_ERR_NULL_POINTER
@@ -430,7 +433,7 @@ def bwd_qk_call(q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, do=A + 4 * SZ, lse=A 
     (dict(Nq=101), fa.FA_ERR_BAD_SHAPE),                  # causal: Nq <= Nk
     (dict(Nq=101, causal=0, ws_bytes=2 * 2 * 101 * 4), fa.FA_ERR_HIP),
     (dict(scale=float("inf")), fa.FA_ERR_BAD_SCALE),
-    (dict(D=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=512), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_bwd_qk_validation_before_any_device_call(kw, expect):
     if expect == fa.FA_ERR_HIP and gpu_visible():

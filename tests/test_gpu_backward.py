@@ -110,9 +110,48 @@ def test_backward_d96(N, causal, dtype):
     _compare(w, g, [(0, 0), (0, 1)], w.scale, f"{w.name} causal={causal}")
 
 
+D256_N = [1, 65, 200, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", D256_N)
+def test_backward_d256(N, causal, dtype):
+    """D = 256 (the dq kernel at one wave per SIMD, dK and dV from the 16-key
+    kernel in 64-key workgroups): every element of both heads, gradients
+    prefilled with NaN."""
+    w = fi.Workload(f"bwd_d256_n{N}_{dtype}", 830 + D256_N.index(N) * 4 + 2 * causal + (dtype == "f16"), 1, 2, N,
+                    256, dtype, causal)
+    gu.log(f"[gpu] backward D=256 N={N} causal={causal} {dtype}")
+    q, k, v = gu.workload_tensors(w)
+    o, lse = fa.attention_forward(q, k, v, causal=causal, scale=w.scale)
+    g = [torch.full_like(q, float("nan")) for _ in range(3)]
+    fa.attention_backward(q, k, v, o, lse, _dout(w), causal=causal, scale=w.scale, dq=g[0], dk=g[1], dv=g[2])
+    torch.cuda.synchronize()
+    _compare(w, g, [(0, 0), (0, 1)], w.scale, f"{w.name} causal={causal}")
+
+
+def test_backward_d256_many_blocks():
+    """D = 256 on a ragged grid of many 64-key workgroups (B=3 H=5 N=333,
+    causal and a negative scale): every element of three heads, gradients
+    prefilled with NaN, and two calls give the same bits."""
+    w = fi.Workload("bwd_d256_b3_h5_n333", 850, 3, 5, 333, 256, "bf16", True)
+    q, k, v = gu.workload_tensors(w)
+    o, lse = fa.attention_forward(q, k, v, causal=True, scale=-w.scale)
+    runs = []
+    for _ in range(2):
+        g = [torch.full_like(q, float("nan")) for _ in range(3)]
+        fa.attention_backward(q, k, v, o, lse, _dout(w), causal=True, scale=-w.scale, dq=g[0], dk=g[1], dv=g[2])
+        torch.cuda.synchronize()
+        runs.append(g)
+    for x, y in zip(*runs):
+        assert torch.equal(x, y)
+    _compare(w, runs[0], [(0, 0), (1, 2), (2, 4)], -w.scale, f"{w.name} scale={-w.scale}")
+
+
 QK_CASES = [(1, 64, 128, True), (17, 200, 64, True), (64, 1000, 128, True), (200, 333, 96, True),
             (129, 130, 128, True), (200, 333, 128, False), (333, 200, 128, False), (1000, 64, 64, False),
-            (65, 4096, 128, True)]
+            (65, 4096, 128, True), (100, 1000, 256, True), (257, 200, 256, False)]
 
 
 @pytest.mark.parametrize("nq,nk,D,causal", QK_CASES, ids=lambda x: str(x))
@@ -253,7 +292,8 @@ def test_backward_f16_negative_scale():
     _compare(w, grads, [(0, 0), (0, 1)], -0.125, f"{w.name} scale=-0.125")
 
 
-@pytest.mark.parametrize("w", [fi.BF16_N4096, fi.CAUSAL_SWEEP[3], fi.F16_N4096, fi.D96_N4096], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [fi.BF16_N4096, fi.CAUSAL_SWEEP[3], fi.F16_N4096, fi.D96_N4096, fi.D256_N4096],
+                         ids=lambda w: w.name)
 def test_backward_full_size(w):
     """The full-size workloads, in the launch configuration the benchmark
     times; every element of seeded heads."""

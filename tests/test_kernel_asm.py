@@ -77,9 +77,11 @@ def test_every_tile_barrier_drains_vmcnt(asm):
 def test_backward_kernels_present(bwd_asm):
     names = [n for n, _ in _kernels(bwd_asm)]
     # (bf16, fp16) x D (64, 96, 128) x causal for each of the three tile kernels (dq, dk/dv, both in
-    # one grid), and (bf16, fp16) x D for the Delta kernel
-    assert sum("bwd_dq" in n for n in names) == 12, names
-    assert sum("bwd_dkdv" in n for n in names) == 12, names
+    # one grid), and (bf16, fp16) x D for the Delta kernel; at D = 256 (bf16, fp16) x causal for the
+    # dq kernel and the 16-key dk/dv kernel
+    assert sum("bwd_dq" in n for n in names) == 16, names
+    assert sum("bwd_dkdv_kernel" in n for n in names) == 12, names
+    assert sum("bwd_dkdv16_kernel" in n for n in names) == 4, names
     assert sum("bwd_fused" in n for n in names) == 12, names
     assert sum("bwd_delta" in n for n in names) == 6, names
 
