@@ -22,6 +22,10 @@
 namespace fa {
 namespace {
 
+// the host's key blocks are the kernels' workgroups
+static_assert(bwd_keys_per_block(128) == kBwdRows && bwd_keys_per_block(256) == 16 * (kBwdThreads / 64),
+              "dk/dv keys per workgroup");
+
 template <typename Kern>
 hipError_t launch(Kern kern, const BwdArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBwdThreads), 0, s, a);

@@ -31,7 +31,7 @@ constexpr int64_t kKeysPerTile = 64;
 
 // Keys per dk/dv workgroup of the backward: 128 (4 waves of 32 keys), or at
 // D = 256 64 (4 waves of 16 keys).
-inline int64_t bwd_keys_per_block(int64_t D) { return D == 256 ? 64 : 128; }
+constexpr int64_t bwd_keys_per_block(int64_t D) { return D == 256 ? 64 : 128; }
 
 // Whether fa_fwd_split runs the one-query-row kernel (Nq = 1, D in {64, 128, 256}).
 inline bool uses_decode_kernel(int64_t Nq, int64_t D) { return Nq == 1 && (D == 64 || D == 128 || D == 256); }

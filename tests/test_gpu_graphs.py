@@ -45,12 +45,14 @@ def _check_replays(run, outs):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("B,H", [(1, 4), (2, 40)], ids=["small_grid", "large_grid"])
-def test_graph_fa_fwd(B, H):
+@pytest.mark.parametrize("B,H,D", [(1, 4, 128), (2, 40, 128), (2, 40, 256)],
+                         ids=["small_grid", "large_grid", "large_grid_d256"])
+def test_graph_fa_fwd(B, H, D):
     """fa_fwd in a graph: a grid that takes the 64-row small-grid kernel (B=1
-    H=4: 28 blocks of 128 rows) and one that takes the 128-row kernel (B=2
-    H=40: 560 blocks)."""
-    w = fi.Workload(f"graph_fwd_b{B}_h{H}", 1100, B, H, 777, 128, "bf16", True)
+    H=4: 28 blocks of 128 rows), one that takes the 128-row kernel (B=2 H=40:
+    560 blocks), and the same grid at D = 256 (the 16-row-wave kernel in
+    128-row workgroups of 8 waves)."""
+    w = fi.Workload(f"graph_fwd_b{B}_h{H}_d{D}", 1100, B, H, 777, D, "bf16", True)
     q, k, v = gu.workload_tensors(w)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, 777), device="cuda")
@@ -69,13 +71,17 @@ def test_graph_fa_fwd_split():
                                                       lse=lse, workspace=ws), [o, lse])
 
 
-def test_graph_fa_bwd():
-    w = fi.Workload("graph_bwd", 1102, 1, 2, 600, 128, "bf16", True)
+@pytest.mark.parametrize("D", [128, 256])
+def test_graph_fa_bwd(D):
+    """fa_bwd in a graph: at D = 128 the small grid takes the one-grid plan
+    (Delta kernel, then both kinds of workgroup), at D = 256 the dq kernel
+    and the 16-key dk/dv kernel."""
+    w = fi.Workload(f"graph_bwd_d{D}", 1102, 1, 2, 600, D, "bf16", True)
     q, k, v = gu.workload_tensors(w)
     do = gu.to_device_bits(fi.full_tensor(w, fi.T_DO), "bf16")
     o, lse = fa.attention_forward(q, k, v, causal=True, scale=w.scale)
     grads = [torch.empty_like(q) for _ in range(3)]
-    st, sz = fa.fa_bwd_query(1, 2, 600, 128, True, fa.FA_DTYPE_BF16)
+    st, sz = fa.fa_bwd_query(1, 2, 600, D, True, fa.FA_DTYPE_BF16)
     ws = torch.empty(sz.workspace_bytes, dtype=torch.uint8, device="cuda")
     _check_replays(lambda: fa.attention_backward(q, k, v, o, lse, do, causal=True, scale=w.scale, dq=grads[0],
                                                  dk=grads[1], dv=grads[2], workspace=ws), grads)
