@@ -642,17 +642,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) 
 //     queries, dO^T and Q^T by transposed reads (two ds_read_b64_tr_b16 per
 //     fragment, the forward's V^T pattern).
 // Each tile is read both ways, so one chunk swizzle serves both patterns:
-// (r3 ^ r4) | r0 << 1 | r1 << 2 | r3 << 3, chosen with a bank model over every
-// lane of both (conflict-free for 8 and 16 lanes a pass of the 16-byte reads,
-// 16 and 32 of the 8-byte ones; 512-byte rows all start on the same bank,
-// and the XOR keeps a chunk within its 256-byte line).  It reads only row
-// bits 0, 1, 3 and 4, which are constant over a lane's reads.
+// the 64-row forward kernel's V swizzle, 2 (r0 | r1 << 1 | r3 << 2), whose
+// transposed reads are known conflict-free.  Measured with the LDS conflict
+// counter, the row reads are conflict-free with it too (512-byte rows all
+// start on the same bank).  An odd swizzle that a bank model of 8-byte reads
+// had passed, (r3 ^ r4) | r0 << 1 | r1 << 2 | r3 << 3, cost 256 conflict
+// cycles per wave and tile in the transposed reads.  The swizzle reads only
+// row bits 0, 1 and 3, which are constant over a lane's reads.
 namespace bwd16 {
 __device__ __forceinline__ int query_of(int b, int t) { return 32 * (b >> 1) + 8 * (t >> 2) + 4 * (b & 1) + (t & 3); }
-__device__ __forceinline__ int swz(int row) {
-  const int r0 = row & 1, r1 = (row >> 1) & 1, r3 = (row >> 3) & 1, r4 = (row >> 4) & 1;
-  return (r3 ^ r4) | (r0 << 1) | (r1 << 2) | (r3 << 3);
-}
+__device__ __forceinline__ int swz(int row) { return 2 * ((row & 3) | (((row >> 3) & 1) << 2)); }
 }  // namespace bwd16
 
 template <typename E, int D, bool CAUSAL>
