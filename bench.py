@@ -23,7 +23,8 @@ the combination of the fp8 and bf16 MFMA peaks (Q K^T runs on the first, P V
 on the second).
 
 With --backward a step is one fa_bwd call (its two kernels: dq with Delta, then
-dk and dv) for a seeded upstream gradient, O and LSE having been computed by
+dk and dv; on small grids a Delta kernel, then one grid of both kinds of
+workgroup) for a seeded upstream gradient, O and LSE having been computed by
 fa_fwd before the timed region.  FLOPs are those of the five products of the
 gradient, 10*B*H*N^2*D (halved when causal): 2.5 times the forward's, whatever
 the kernels recompute.
