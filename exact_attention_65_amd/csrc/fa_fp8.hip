@@ -8,13 +8,14 @@
 #include "fa_check.h"
 #include "fa_device.h"
 #include "fa_fp8_kernel.hpp"
+#include "fa_fp8_rows16_kernel.hpp"
 
 namespace fa {
 namespace {
 
 template <typename Kern>
-hipError_t launch(Kern kern, const Fp8Args& a, hipStream_t s) {
-  hipLaunchKernelGGL(kern, dim3(a.n_blocks), dim3(kFp8Threads), 0, s, a);
+hipError_t launch(Kern kern, const Fp8Args& a, hipStream_t s, int threads = kFp8Threads) {
+  hipLaunchKernelGGL(kern, dim3(a.n_blocks), dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -54,7 +55,9 @@ __attribute__((visibility("default"))) fa_status fa_fwd_fp8(const void* q, const
   a.qflip = std::signbit(scale) && scale != 0.0f ? 0x80808080u : 0u;
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (D == 256) e = causal ? fa::launch(fa::fa_fwd_fp8_kernel<256, true>, a, s) : fa::launch(fa::fa_fwd_fp8_kernel<256, false>, a, s);
+  // D = 256: 16 query rows per wave, two waves per SIMD (the same 128-row blocks)
+  if (D == 256) e = causal ? fa::launch(fa::fa_fwd_fp8_rows16_kernel<true>, a, s, 512)
+                           : fa::launch(fa::fa_fwd_fp8_rows16_kernel<false>, a, s, 512);
   else if (D == 128) e = causal ? fa::launch(fa::fa_fwd_fp8_kernel<128, true>, a, s) : fa::launch(fa::fa_fwd_fp8_kernel<128, false>, a, s);
   else e = causal ? fa::launch(fa::fa_fwd_fp8_kernel<64, true>, a, s) : fa::launch(fa::fa_fwd_fp8_kernel<64, false>, a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
