@@ -54,26 +54,19 @@ namespace fp8 {
 // lanes by a bank model; the row shift swizzle of half rows, (row >> 1) & 7,
 // left the score reads 2-way conflicted in the 8-lane case, which the
 // conflict counter showed).
-//
-// At D = 256 (16 chunks a row) the swizzle is swap23 of the row's bits 0-3: a
-// bijection on the 16 rows of a 16-lane score read whose low 3 bits also
-// differ on each 8-lane half (rows 0-3 with 8-11, 4-7 with 12-15).
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 256) return swap23(row & 15);
-  else if constexpr (D == 128) return ((row >> 1) & 1) | (((row ^ (row >> 2)) & 1) << 1) | (((row >> 3) & 1) << 2);
+  if constexpr (D == 128) return ((row >> 1) & 1) | (((row ^ (row >> 2)) & 1) << 1) | (((row >> 3) & 1) << 2);
   else return (((row >> 1) ^ (row >> 2)) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1);
 }
-// Quarter of the row (D/4 values: one MX block at D <= 128, two at D = 256)
-// that lane (r, k) converts: row r of the wave's 16, k = lane / 16.  The XOR
-// with bits of r makes the 16-byte bf16 writes of the conversion 2-way
-// conflicted at most (the least possible for writes of one chunk position per
-// instruction, given the bf16 tile's swizzle) and keeps the E4M3 reads
-// conflict-free; at D = 256 the tile swizzle alone does that.
+// Quarter of the row (D/4 values, at most one MX block) that lane (r, k)
+// converts: row r of the wave's 16, k = lane / 16.  The XOR with bits of r
+// makes the 16-byte bf16 writes of the conversion 2-way conflicted at most
+// (the least possible for writes of one chunk position per instruction, given
+// the bf16 tile's swizzle) and keeps the E4M3 reads conflict-free.
 template <int D>
 __device__ __forceinline__ int cv_part(int r, int k) {
-  if constexpr (D == 256) return k;
-  else if constexpr (D == 128) return k ^ (((r >> 2) & 1) << 1);
+  if constexpr (D == 128) return k ^ (((r >> 2) & 1) << 1);
   else return k ^ ((r >> 1) & 3);
 }
 // Order of a converting lane's two 8-byte halves of each E4M3 chunk (1:
@@ -84,20 +77,14 @@ __device__ __forceinline__ int cv_part(int r, int k) {
 // 2-way), and the 8-byte reads conflict-free.
 template <int D>
 __device__ __forceinline__ int cv_swap(int r) {
-  if constexpr (D == 256) return ((r >> 2) ^ (r >> 3)) & 1;
-  else if constexpr (D == 128) return (r >> 2) & 1;
+  if constexpr (D == 128) return (r >> 2) & 1;
   else return (r ^ (r >> 3)) & 1;
 }
 // A row's D/32 scale bytes as one word (read as 4-byte words: the scale
 // arrays are 4-byte aligned); rows past N read as scale 1 (code 127).
 template <int D>
-using scale_word_t = typename std::conditional<(D > 128), uint64_t, uint32_t>::type;
-template <int D>
-__device__ __forceinline__ scale_word_t<D> scale_word(const uint8_t* p, bool valid) {
-  if constexpr (D == 256) {
-    if (!valid) return 0x7F7F7F7F7F7F7F7Full;
-    return (uint64_t)((const uint32_t*)p)[0] | ((uint64_t)((const uint32_t*)p)[1] << 32);
-  } else if constexpr (D == 128) {
+__device__ __forceinline__ uint32_t scale_word(const uint8_t* p, bool valid) {
+  if constexpr (D == 128) {
     return valid ? *(const uint32_t*)p : 0x7F7F7F7Fu;
   } else {
     return valid ? (uint32_t) * (const uint16_t*)p : 0x7F7F7F7Fu;
@@ -123,10 +110,10 @@ __device__ __forceinline__ uint32_t addr(int row, int chunk) {
 // of iteration j); the barrier of iteration j+1 publishes it to the value MFMAs
 // of iteration j+1.  So each tile costs one barrier, as in the bf16 kernel.
 //
-// D = 256 holds 128 output registers per lane and 128 KB of tiles: one
-// workgroup per CU, one wave per SIMD.
+// D = 64 and 128; D = 256 runs on fa_fwd_fp8_rows16_kernel, whose 16-row
+// waves fit two to a SIMD where 32-row ones need a SIMD each.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFp8Threads, D == 256 ? 1 : 2) void fa_fwd_fp8_kernel(Fp8Args a) {
+__global__ __launch_bounds__(kFp8Threads, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
   constexpr int BN = 64;
   constexpr int CPR = D / 16;          // 16-byte chunks per E4M3 row
   constexpr int TILE16 = BN * CPR;     // 16-byte chunks per E4M3 tile
@@ -145,18 +132,13 @@ __global__ __launch_bounds__(kFp8Threads, D == 256 ? 1 : 2) void fa_fwd_fp8_kern
   constexpr int CPRH = D / 8;          // 16-byte chunks per bf16 row
   constexpr int VPL = D / 4;           // V values one lane converts per tile
   constexpr int NCH = VPL / 16;        // E4M3 chunks one lane converts per tile
-  constexpr int NVB = (VPL + 31) / 32; // MX blocks among them
   constexpr int G0 = NSB / 4;          // phase B slot of the first conversion group
-  // D = 256: the block scales of a tile come into LDS with its codes instead
-  // of into registers two tiles ahead (registers are short there)
-  constexpr bool kScalesLds = D == 256;
+  static_assert(D == 64 || D == 128, "head dimensions");
   static_assert(NLD >= 1 && RPB * CPR == 64 && NKB == 2 && NP % NSA == 0, "tile shape");
   static_assert(G0 >= 2 && G0 + 4 * NCH < NSB, "conversion slots");
 
   __shared__ u32x4 kA[TILE16], kB[TILE16], vA[TILE16], vB[TILE16];  // E4M3 tiles
   __shared__ u32x4 wA[BN * CPRH], wB[BN * CPRH];                     // bf16 V tiles
-  constexpr int SCW = kScalesLds ? BN * NSC / 4 : 1;                // scale dwords of a tile
-  __shared__ uint32_t ksA[SCW], ksB[SCW], vsA[SCW], vsB[SCW];        // K / V block scales
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -182,21 +164,17 @@ __global__ __launch_bounds__(kFp8Threads, D == 256 ? 1 : 2) void fa_fwd_fp8_kern
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int i = tid; i < TILE16; i += kFp8Threads) kA[i] = kB[i] = vA[i] = vB[i] = z;
-    if constexpr (kScalesLds)
-      for (int i = tid; i < SCW; i += kFp8Threads) ksA[i] = ksB[i] = vsA[i] = vsB[i] = 0u;
   }
 
   // Q as the B operand of the score MFMA: for step ks, bytes 0..15 are
   // Q[qrow][64ks + 16h .. +15] and bytes 16..31 Q[qrow][64ks + 32 + 16h .. +15]
   // (the instruction's first and second 32-wide block of the step); the lane
   // supplies the scale of block 2ks + h of its row.
-  // (At D = 256 the four scale bytes are packed into one register, byte ks
-  // for step ks.)
   i32x8 qf[NKS];
-  int qsc[D == 256 ? 1 : NKS];
+  int qsc[NKS];
   {
     const u32x4 fl = {a.qflip, a.qflip, a.qflip, a.qflip};
-    const fp8::scale_word_t<D> sdw = fp8::scale_word<D>(QSg + (size_t)qrow * NSC, qrow < N);
+    const uint32_t sdw = fp8::scale_word<D>(QSg + (size_t)qrow * NSC, qrow < N);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
@@ -207,9 +185,7 @@ __global__ __launch_bounds__(kFp8Threads, D == 256 ? 1 : 2) void fa_fwd_fp8_kern
       }
       const i32x8 f = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       qf[ks] = f;
-      const int b = (int)((sdw >> (8 * (2 * ks + h))) & 0xFFu);
-      if constexpr (D == 256) qsc[0] = ks == 0 ? b : qsc[0] | (b << (8 * ks));
-      else qsc[ks] = b;
+      qsc[ks] = (int)((sdw >> (8 * (2 * ks + h))) & 0xFFu);
     }
   }
 
@@ -228,7 +204,7 @@ __global__ __launch_bounds__(kFp8Threads, D == 256 ? 1 : 2) void fa_fwd_fp8_kern
   };
 
   // V conversion: row 16 wave + lane % 16 of the tile, values d0 .. d0 + VPL - 1
-  // (NVB whole MX blocks), written as bf16 in the bf16 kernel's V layout
+  // (within one MX block), written as bf16 in the bf16 kernel's V layout
   const int cv_row = wave * 16 + (lane & 15);
   const int cv_d0 = fp8::cv_part<D>(lane & 15, lane >> 4) * VPL;
   const int cv_s = fp8::cv_swap<D>(lane & 15);
@@ -236,51 +212,27 @@ __global__ __launch_bounds__(kFp8Threads, D == 256 ? 1 : 2) void fa_fwd_fp8_kern
   // block scales of a tile, loaded into registers two tiles ahead (a row's
   // D/32 bytes need not fill whole dwords, so they do not go through the
   // 4-byte tile loads): the K scale bytes of this lane's two score rows, and
-  // the V scale bytes of the NVB blocks this lane converts; rows past N read
-  // as 1
-  // With kScalesLds the struct names the tile's LDS scale rows instead: row r
-  // of the tile at bytes 8r .. 8r + 7, loaded by buffer-to-LDS loads (waves
-  // 0-1 the K rows, waves 2-3 the V rows, 256 bytes each); rows past N are
-  // never loaded and keep finite codes (zero, or an earlier tile's).
+  // the V scale byte of the block this lane converts; rows past N read as 1
   struct TileScales {
-    fp8::scale_word_t<D> k[2];
+    uint32_t k[2];
     uint32_t v;
-    uint32_t* kl;
-    uint32_t* vl;
   };
   auto load_scales = [&](TileScales& ts, int kv0) __attribute__((always_inline)) {
-    if constexpr (kScalesLds) {
-      const int part = wave & 1;
-      const uint8_t* src = (wave < 2 ? KSg : VSg) + (size_t)kv0 * NSC;
-      uint32_t* dst = (wave < 2 ? ts.kl : ts.vl) + 64 * part;
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)src, (short)0, (int)((uint32_t)(N - kv0) * NSC), kRsrcWord3);
-      lds_load4(r, (float*)dst, (uint32_t)(256 * part + 4 * lane));
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = kv0 + 32 * kb + swap23(c32);
-        ts.k[kb] = fp8::scale_word<D>(KSg + (size_t)row * NSC, row < N);
-      }
-      const int vrow = kv0 + cv_row;
-      const uint8_t* vs = VSg + (size_t)vrow * NSC + cv_d0 / 32;
-      if constexpr (NVB == 2) ts.v = vrow < N ? (uint32_t)vs[0] | ((uint32_t)vs[1] << 8) : 0x7F7Fu;
-      else ts.v = vrow < N ? (uint32_t)vs[0] : 127u;
-    }
-  };
-  // the K scale words of this lane's two score rows, and the V scale bytes of
-  // the blocks it converts
-  auto k_scales = [&](const TileScales& ts, fp8::scale_word_t<D> (&kw)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      if constexpr (kScalesLds) kw[kb] = *(const fp8::scale_word_t<D>*)((const char*)ts.kl + 8 * (32 * kb + swap23(c32)));
-      else kw[kb] = ts.k[kb];
+      const int row = kv0 + 32 * kb + swap23(c32);
+      ts.k[kb] = fp8::scale_word<D>(KSg + (size_t)row * NSC, row < N);
     }
+    const int vrow = kv0 + cv_row;
+    ts.v = vrow < N ? (uint32_t)VSg[(size_t)vrow * NSC + cv_d0 / 32] : 127u;
   };
-  auto v_scales = [&](const TileScales& ts) __attribute__((always_inline)) {
-    if constexpr (kScalesLds) return (uint32_t) * (const uint16_t*)((const char*)ts.vl + NSC * cv_row + cv_d0 / 32);
-    else return ts.v;
+  // the K scale words of this lane's two score rows, and the V scale byte of
+  // the block it converts
+  auto k_scales = [&](const TileScales& ts, uint32_t (&kw)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) kw[kb] = ts.k[kb];
   };
+  auto v_scales = [&](const TileScales& ts) __attribute__((always_inline)) { return ts.v; };
 
   // K operand of score MFMA (kb, ks): rows 32kb + swap23(c32), E4M3 chunks
   // 4ks + h (bytes 0..15) and 4ks + 2 + h (bytes 16..31).  With the row's
@@ -336,13 +288,13 @@ __global__ __launch_bounds__(kFp8Threads, D == 256 ? 1 : 2) void fa_fwd_fp8_kern
 
   // scores of one tile: NSA scaled FP8 MFMAs (the scale byte of K row
   // 32kb + swap23(c32), block 2ks + h, from the tile's scale dwords)
-  auto score_mfma = [&](f32x16 (&s)[NKB], const i32x8& kf, const fp8::scale_word_t<D> (&kw)[2], int m)
+  auto score_mfma = [&](f32x16 (&s)[NKB], const i32x8& kf, const uint32_t (&kw)[2], int m)
       __attribute__((always_inline)) {
     const int kb = m / NKS, ks = m % NKS;
     const int ksc = (int)((kw[kb] >> (8 * (2 * ks + h))) & 0xFFu);
     const f32x16 z = {};
     s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[ks], ks == 0 ? z : s[kb], 0, 0, 0, ksc, 0,
-                                                            D == 256 ? (qsc[0] >> (8 * ks)) & 0xFF : qsc[ks]);
+                                                            qsc[ks]);
   };
   // element (kb, i) of tile j holds key j*BN + 32kb + 8h + kofs(i) of query qrow
   auto mask = [&](f32x16 (&s)[NKB], int j) __attribute__((always_inline)) {
@@ -420,8 +372,7 @@ __global__ __launch_bounds__(kFp8Threads, D == 256 ? 1 : 2) void fa_fwd_fp8_kern
   };
   auto conv_group = [&](uint32_t vsw, int g) __attribute__((always_inline)) {
     const int cch = g >> 2, e = g & 3;
-    // chunk cch (16 values) lies in block cch / 2 of the lane's NVB
-    const uint32_t vb = NVB == 2 ? (vsw >> (8 * (cch >> 1))) & 0xFFu : vsw;
+    const uint32_t vb = vsw;  // the lane's values lie in one MX block
     const float sc = __builtin_bit_cast(float, vb << 23);
     const int w = (int)cin[cch][e];
     uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, sc, false));
@@ -459,7 +410,7 @@ __global__ __launch_bounds__(kFp8Threads, D == 256 ? 1 : 2) void fa_fwd_fp8_kern
   auto phase_a = [&](f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], const u32x4* Kt, const TileScales& ts)
       __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
-    fp8::scale_word_t<D> kw[2];
+    uint32_t kw[2];
     k_scales(ts, kw);
     i32x8 kf[NSA];
     kf[0] = kfrag(Kt, 0);
@@ -531,10 +482,6 @@ __global__ __launch_bounds__(kFp8Threads, D == 256 ? 1 : 2) void fa_fwd_fp8_kern
 
   // ---- prologue --------------------------------------------------------------
   TileScales tsA, tsB;  // scales of the tiles whose K / V codes are in kA, vA and kB, vB
-  tsA.kl = ksA;
-  tsA.vl = vsA;
-  tsB.kl = ksB;
-  tsB.vl = vsB;
   __syncthreads();  // zeroed tiles visible before any load lands
   if (n_tiles > 0) {
     issue(kA, Kg, 0);
@@ -550,7 +497,7 @@ __global__ __launch_bounds__(kFp8Threads, D == 256 ? 1 : 2) void fa_fwd_fp8_kern
   __syncthreads();  // tiles 0 and 1 in LDS
   if (n_tiles > 0) convert_all(vA, wA, tsA);
   if (n_vis > 0) {
-    fp8::scale_word_t<D> kw[2];
+    uint32_t kw[2];
     k_scales(tsA, kw);
     i32x8 kf[NSA];
     kf[0] = kfrag(kA, 0);
