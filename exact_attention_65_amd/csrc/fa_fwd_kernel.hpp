@@ -66,7 +66,7 @@ struct FwdArgs {
   int nk;         // key / value rows per (b, h); nq <= nk under the causal mask
   int n_bh;       // B * H
   int n_qblk;     // query blocks per (b, h): ceil(nq / rows per workgroup)
-  int n_split;    // workgroups that share the keys of one query block (bf16 only)
+  int n_split;    // workgroups that share the keys of one query block (16-bit types only)
   int n_blocks;   // workgroups in the grid: n_bh * n_qblk * n_split
   float c;        // |scale| * log2(e), at least FLT_MIN
   uint32_t qflip; // XOR mask applied to Q's bits: flips every sign when scale < 0
